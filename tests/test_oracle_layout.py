@@ -1,0 +1,139 @@
+"""Pins for the oracle's cache layout, tile map and pair counts (CPU only), and for the
+synthetic workloads against the facts the pages fix (tests/golden/page_facts.json)."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import layout as L
+from block_causal_attention_qi_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- tile map
+
+def test_tile_map_worked_example():
+    """Blocks text 3, ref 5, image 4 (offsets 0, 3, 8, 12); bm = bn = 4.
+    Key tiles [0,4) [4,8) [8,12).  Row tiles: text [0,3); ref [3,7) [7,8); image [8,12).
+    Text rows see keys < 3, ref rows keys < 8, image rows all 12 keys."""
+    bl = [3, 5, 4]
+    full = L.tile_map(bl, L.CALL_FULL, 4, 4).ravel().tolist()
+    assert full == [1, 0, 0,  2, 2, 0,  2, 2, 0,  2, 2, 2]
+    pre = L.tile_map(bl, L.CALL_PREFIX, 4, 4).ravel().tolist()
+    assert pre == [1, 0,  2, 2,  2, 2]
+    den = L.tile_map(bl, L.CALL_DENOISE, 4, 4).ravel().tolist()
+    assert den == [2, 2, 2]
+    # bn = 5: key tiles [0,5) [5,10) [10,12); ref rows see keys < 8 -> FULL, PARTIAL, EMPTY
+    assert L.tile_map(bl, L.CALL_FULL, 4, 5).ravel().tolist() == \
+        [1, 0, 0,  2, 1, 0,  2, 1, 0,  2, 2, 2]
+
+
+@pytest.mark.parametrize("bl", [[32, 64, 64], [445, 4096, 4096, 4096], [7, 1, 3, 130],
+                                [1, 1, 1], [300]])
+@pytest.mark.parametrize("bm,bn", [(128, 64), (64, 64), (16, 32), (128, 128)])
+def test_tile_map_closed_form(bl, bm, bn):
+    """Row tiles lie in one block b, whose rows see keys [0, o_{b+1}); a key tile [k0, k1)
+    is FULL iff k1 <= o_{b+1}, EMPTY iff k0 >= o_{b+1}, else PARTIAL."""
+    if len(bl) == 1 and bl[0] == 300:
+        calls = [L.CALL_FULL]
+    else:
+        calls = [L.CALL_PREFIX, L.CALL_DENOISE, L.CALL_FULL]
+    ends = np.cumsum(bl)
+    for call in calls:
+        if call == L.CALL_PREFIX and len(bl) < 2:
+            continue
+        got = L.tile_map(bl, call, bm, bn)
+        nkeys = int(ends[-2]) if call == L.CALL_PREFIX else int(ends[-1])
+        tiles = L.row_tiles(bl, call, bm)
+        assert got.shape == (len(tiles), -(-nkeys // bn))
+        for i, (r0, nr) in enumerate(tiles):
+            e = int(ends[np.searchsorted(ends, r0, side="right")])
+            assert int(ends[np.searchsorted(ends, r0 + nr - 1, side="right")]) == e
+            for j in range(got.shape[1]):
+                k0, k1 = j * bn, min(nkeys, (j + 1) * bn)
+                want = 2 if k1 <= e else (0 if k0 >= e else 1)
+                assert got[i, j] == want
+
+
+def test_row_tiles_cover_call_rows_once():
+    bl = [445, 4096, 4096, 4096]
+    for call, (lo, hi) in ((L.CALL_PREFIX, (0, 445 + 8192)), (L.CALL_DENOISE, (445 + 8192, sum(bl))),
+                           (L.CALL_FULL, (0, sum(bl)))):
+        rows = np.concatenate([np.arange(r0, r0 + n) for r0, n in L.row_tiles(bl, call, 128)])
+        assert np.array_equal(rows, np.arange(lo, hi))
+
+
+# ---------------------------------------------------------------- pair / FLOP counts
+
+def test_useful_pairs_closed_form():
+    for bl in ([32, 64, 64], [256, 4096], [3, 5, 4], [256] + [4096] * 5):
+        ends = np.cumsum(bl)
+        lp, n = int(ends[-2]), int(ends[-1])
+        full = sum(int(b) * int(e) for b, e in zip(bl, ends))
+        assert L.useful_pairs(bl, L.CALL_FULL) == full
+        assert L.useful_pairs(bl, L.CALL_DENOISE) == bl[-1] * n
+        assert L.useful_pairs(bl, L.CALL_PREFIX) == full - bl[-1] * n
+        assert lp == n - bl[-1]
+
+
+def test_flops_of_the_named_workloads():
+    t2i = synth.WORKLOADS["t2i1024"]
+    # image rows see the 256-token prompt plus all 4096 image tokens
+    assert L.useful_pairs(t2i.requests[0], L.CALL_DENOISE) == 4096 * 4352
+    assert L.useful_flops(t2i.requests, L.CALL_DENOISE, 24, 128) == 4 * 128 * 24 * 4096 * 4352
+    e4 = synth.WORKLOADS["edit4"]
+    den = L.useful_flops(e4.requests, L.CALL_DENOISE, 24, 128)
+    full = L.useful_flops(e4.requests, L.CALL_FULL, 24, 128)
+    assert den == 4 * 128 * 24 * 4096 * 20736
+    assert 3.0 < full / den < 3.05
+
+
+# ---------------------------------------------------------------- cache layout
+
+def test_cache_layout_worked_example():
+    # one request, prefix 3 + 5 = 8 tokens, H = 2, D = 64
+    regs, total = L.cache_layout([[3, 5, 4]], 2, 64, L.KV_BF16)
+    assert (regs[0]["k_off"], regs[0]["v_off"], regs[0]["s_off"], total) == (0, 2048, None, 4096)
+    assert L.cache_offset(regs, 64, L.KV_BF16, 0, 1, 1, 3) == 2048 + (8 + 3) * 64 * 2
+    regs, total = L.cache_layout([[3, 5, 4], [2, 6]], 2, 64, L.KV_FP8)
+    assert [(r["k_off"], r["v_off"], r["s_off"], r["end"]) for r in regs] == \
+        [(0, 1024, 2048, 2064), (2304, 2560, 2816, 2832)]
+    assert total == 3072
+    assert L.cache_offset(regs, 64, L.KV_FP8, 1, 0, 1, 1) == 2304 + (2 + 1) * 64
+    # parts that do not end on a 256-byte boundary: H = 1, D = 64, prefix 3 tokens
+    regs, total = L.cache_layout([[3, 4]], 1, 64, L.KV_FP8)
+    assert (regs[0]["v_off"], regs[0]["s_off"], regs[0]["end"], total) == (256, 512, 520, 768)
+    regs, total = L.cache_layout([[3, 4]], 1, 64, L.KV_BF16)
+    assert (regs[0]["v_off"], regs[0]["end"], total) == (512, 896, 1024)
+
+
+# ---------------------------------------------------------------- page facts
+
+@pytest.fixture(scope="module")
+def facts():
+    with open(os.path.join(GOLDEN, "page_facts.json")) as f:
+        return {k: v for k, v in json.load(f).items() if not k.startswith("_")}
+
+
+def test_workload_shapes_follow_the_pages(facts):
+    f = facts["autoencoder_spatial_factor"]["value"]
+    tokens = lambda side: (side // f) * (side // f)
+    W = synth.WORKLOADS
+    assert W["t2i1024"].requests[0][-1] == tokens(1024)
+    assert W["edit2048"].requests[0][-1] == tokens(2048)
+    ref_tokens = tokens(facts["reference_area_side"]["value"])
+    assert all(b == ref_tokens for b in W["edit4"].requests[0][1:-1])
+    assert len(W["edit4"].requests[0]) - 2 == facts["max_references_vllm_omni"]["value"]
+    assert len(W["wave8"].requests) == facts["step_batch_max_num_seqs"]["value"]
+    assert max(W["wave8"].n_refs) <= facts["max_references_vllm_omni"]["value"]
+    assert all(w.steps == facts["denoising_steps"]["value"] for k, w in W.items() if k != "tiny")
+    assert all(w.layers == facts["dit_layers"]["value"] for k, w in W.items() if k != "tiny")
+    assert 1024 % facts["output_side_multiple"]["value"] == 0
+
+
+def test_four_reference_recompute_fraction(facts):
+    fr = facts["four_reference_recompute_fraction"]
+    bl = synth.WORKLOADS["edit4"].requests[0]
+    assert abs(bl[-1] / sum(bl) - fr["value"]) <= fr["tolerance"]
