@@ -1,0 +1,251 @@
+"""Benchmark of prefix-reuse block-causal attention on one MI355X.
+
+One step = one denoising step of the DiT's attention: qi_denoise_attn_step on each of
+the 32 layers, every layer with its own prefix cache and its own Q/K/V/O buffers (so
+the timed work is not served from a warm cache of one layer's data).  Inputs are resident
+in HBM before timing starts; the prefix caches are built (step 0) before the timed region
+and the build itself is timed separately.
+
+Prints ONE JSON line.  `value` is useful attention TFLOP/s (4*D*H*allowed pairs; masked
+pairs are not counted) on the 1024x1024 text-to-image workload (24 heads x 128, text 256
++ image 4096 tokens); the 2048x2048 edit and the others are reported under "extra".
+
+    python bench.py [--steps K] [--warmup W] [--workload t2i1024] [--extra] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "block-causal attn TFLOP/s & % MFMA peak per denoise step (1024^2, 2048^2)"
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published (no sparsity)
+KERNEL_SRC = os.path.join(ROOT, "block_causal_attention_qi_amd", "csrc", "attn_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_denoise_t2i1024_traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_sha():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+class Layers:
+    """Per-layer device buffers of one workload: layer l holds the base inputs rolled by
+    97*l tokens (same distribution, different bytes)."""
+
+    def __init__(self, name, layers, dev, need_full=False):
+        import torch
+        from block_causal_attention_qi_amd import qi, synth
+        self.w = synth.WORKLOADS[name]
+        w = self.w
+        t0 = time.time()
+        x = synth.generate(w, steps=1)
+        log("[bench] %s: inputs drawn in %.1fs" % (name, time.time() - t0))
+        b = lambda a: synth.to_bf16(a, dev)
+        base = dict(q_pre=b(x.q_pre), k_pre=b(x.k_pre), v_pre=b(x.v_pre), q_img=b(x.q_img[0]),
+                    k_img=b(x.k_img[0]), v_img=b(x.v_img[0]))
+        if need_full:
+            base.update(zip(("q_all", "k_all", "v_all"), (b(t) for t in x.full(0))))
+        del x
+        self.plan = qi.Plan(w.requests, w.n_heads, w.head_dim, w.kv_dtype)
+        self.ws = torch.empty(max(256, self.plan.workspace_bytes), dtype=torch.uint8, device=dev)
+        qi.qi_plan_upload(self.plan, self.ws)
+        self.layers = []
+        for l in range(layers):
+            sh = 97 * l
+            t = {k: torch.roll(v, shifts=sh, dims=0).contiguous() for k, v in base.items()}
+            t["cache"] = torch.empty(self.plan.cache_bytes, dtype=torch.uint8, device=dev)
+            t["o_pre"] = torch.empty_like(t["q_pre"])
+            t["o_img"] = torch.empty_like(t["q_img"])
+            if need_full:
+                t["o_all"] = torch.empty_like(t["q_all"])
+            self.layers.append(t)
+        del base
+        torch.cuda.synchronize()
+
+    def build(self):
+        from block_causal_attention_qi_amd import qi
+        for t in self.layers:
+            qi.qi_prefix_kv_build(self.plan, t["q_pre"], t["k_pre"], t["v_pre"], t["o_pre"],
+                                  t["cache"])
+
+    def denoise(self):
+        from block_causal_attention_qi_amd import qi
+        for t in self.layers:
+            qi.qi_denoise_attn_step(self.plan, t["cache"], t["q_img"], t["k_img"], t["v_img"],
+                                    t["o_img"])
+
+    def full(self):
+        from block_causal_attention_qi_amd import qi
+        for t in self.layers:
+            qi.qi_attn_full_reference_step(self.plan, t["q_all"], t["k_all"], t["v_all"],
+                                           t["o_all"])
+
+
+def timed(fn, steps, warmup):
+    """Warm up, then time exactly `steps` calls of fn with HIP events on the current
+    stream (the stream libqi launches on), synchronising on both sides."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e)   # ms
+
+
+def measure(name, steps, warmup, layers, dev, with_full=False, with_build=True):
+    from block_causal_attention_qi_amd import qi
+    L = Layers(name, layers, dev, need_full=with_full)
+    flops = qi.useful_flops(L.plan, qi.QI_CALL_DENOISE)
+    res = {"workload": name, "requests": L.w.requests, "heads": L.w.n_heads,
+           "head_dim": L.w.head_dim, "kv_cache": L.w.kv_dtype, "layers": layers,
+           "denoise_gflop_per_layer": flops / 1e9}
+    L.build()   # step 0 of every layer (untimed here: the caches must exist)
+    ms = timed(L.denoise, steps, warmup)
+    per_launch = ms / (steps * layers)
+    res.update(ms_per_step=ms / steps, ms_per_layer_step=per_launch,
+               tflops=flops / (per_launch * 1e-3) / 1e12)
+    res["frac_of_peak"] = res["tflops"] / PEAK_BF16_TFLOPS
+    if with_build:
+        bflops = qi.useful_flops(L.plan, qi.QI_CALL_PREFIX)
+        bms = timed(L.build, max(1, steps // 2), 1) / (max(1, steps // 2) * layers)
+        res.update(build_ms_per_layer=bms, build_prefix_tflops=bflops / (bms * 1e-3) / 1e12)
+    if with_full:
+        fflops = qi.useful_flops(L.plan, qi.QI_CALL_FULL)
+        fms = timed(L.full, max(1, steps // 2), 1) / (max(1, steps // 2) * layers)
+        res.update(full_ms_per_layer=fms, full_tflops=fflops / (fms * 1e-3) / 1e12,
+                   cached_speedup_vs_full=fms / per_launch)
+    if L.w.kv_dtype == "fp8":
+        # compulsory bytes of one denoising launch: image Q/K/V read + O written (bf16)
+        # plus the fp8 prefix cache read once
+        pre, img, _ = qi.qi_plan_tokens(L.plan)
+        hd = L.w.n_heads * L.w.head_dim
+        byts = 4 * img * hd * 2 + 2 * pre * hd + 8 * L.w.n_heads * len(L.w.requests)
+        res["compulsory_gb_per_s"] = byts / (per_launch * 1e-3) / 1e9
+    del L
+    import torch
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(name):
+    """The fp64 oracle (oracle/attention.py, untuned) on one layer-step of the cached
+    denoising call, all heads and rows, on the host cores."""
+    import numpy as np
+    from block_causal_attention_qi_amd import synth
+    from oracle import attention as A
+    from oracle import layout as OL
+    w = synth.WORKLOADS[name]
+    x = synth.generate(w, steps=1)
+    e = lambda a: synth.bf16_exact(a)
+    bl = w.requests[0]
+    args = (e(x.q_img[0]), e(x.k_pre), e(x.v_pre), e(x.k_img[0]), e(x.v_img[0]))
+    t0 = time.perf_counter()
+    A.denoise_step(bl, *args)
+    dt = time.perf_counter() - t0
+    flops = OL.useful_flops(w.requests, OL.CALL_DENOISE, w.n_heads, w.head_dim)
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads") or 0) for i in threadpool_info()) or None
+    except Exception:
+        pass
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads or os.cpu_count(),
+            "kind": "oracle", "seconds": dt,
+            "sample": "one layer-step of the denoising call of %s (all %d heads, all %d image "
+                      "rows), float64 NumPy oracle" % (name, w.n_heads, w.image_lens[0])}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--layers", type=int, default=32)
+    ap.add_argument("--workload", default="t2i1024")
+    ap.add_argument("--extra", action="store_true",
+                    help="also time edit2048, edit4 (cached vs full) and wave8 (fp8)")
+    ap.add_argument("--no-extra", action="store_true", help="time only the main workload")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(heads or requests would shard with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    from block_causal_attention_qi_amd import qi  # noqa: F401  (fails loudly if not built)
+
+    main_res = measure(a.workload, a.steps, a.warmup, a.layers, dev, with_full=False)
+    log("[bench] %s" % json.dumps(main_res))
+    extra = {}
+    if not a.no_extra:
+        names = ["edit2048"] + (["edit4", "wave8"] if a.extra else [])
+        for n in names:
+            if n == a.workload:
+                continue
+            extra[n] = measure(n, max(2, a.steps // 2), 1, a.layers, dev, with_full=(n == "edit4"))
+            log("[bench] %s" % json.dumps(extra[n]))
+
+    traffic = None
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        if rec.get("kernel_source_sha256") == kernel_sha() and rec.get("workload") == a.workload:
+            traffic = rec["hbm_bytes_per_launch"]
+    except (OSError, ValueError, KeyError):
+        pass
+    flops_launch = main_res["denoise_gflop_per_layer"] * 1e9
+    achieved = main_res["tflops"]
+    out = {
+        "metric": METRIC,
+        "value": round(achieved, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(main_res["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": a.workload, "blocks": main_res["requests"],
+                   "heads": main_res["heads"], "head_dim": main_res["head_dim"],
+                   "layers": a.layers, "kv_cache": main_res["kv_cache"],
+                   "step": "qi_denoise_attn_step on each of %d layers" % a.layers},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "kernel": "attn_fwd_kernel<128, bf16 cache>",
+                     "flop_per_launch": flops_launch,
+                     "ms_per_launch": round(main_res["ms_per_layer_step"], 5)},
+        "extra": extra,
+    }
+    if not a.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(a.workload)
+        log("[bench] cpu baseline %s" % json.dumps(out["cpu_baseline"]))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,337 @@
+// Host side of libqi: wave validation, block offsets, row tiles, XCD-aware launch
+// schedules, prefix-cache layout, tile classification and pair counts.  No HIP calls.
+//
+// The block structure follows the pages: a request is a text-instruction block, then its
+// reference-image blocks in the order given, then the image-latent block (ThakiCloud blog
+// "Qwen-Image-2.1 vLLM-Omni day 0", section "Serving architecture: the cross-step prefix
+// KV cache"; vLLM recipe "Qwen/Qwen-Image-2.1", section "Offline inference" for the
+// reference order).  A wave is a set of requests at the same denoising phase (recipe,
+// section "Online serving").
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <numeric>
+
+#include "qi_internal.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Rows of a call for one request: list of (first row, row count) blocks, and key count.
+void call_blocks(const qi_req_host &r, int call, std::vector<std::pair<int, int>> &blocks,
+                 int &nkeys) {
+  const int nb = (int)r.bl.size();
+  int b0 = 0, b1 = nb;
+  if (call == QI_CALL_PREFIX) {
+    b1 = nb - 1;
+    nkeys = r.lp;
+  } else if (call == QI_CALL_DENOISE) {
+    b0 = nb - 1;
+    nkeys = r.n;
+  } else {
+    nkeys = r.n;
+  }
+  blocks.clear();
+  for (int b = b0; b < b1; ++b) blocks.emplace_back((int)r.off[b], r.bl[b]);
+}
+
+// Rows of a row tile [r0, r0 + nr) all lie in one block b; they see keys [0, off[b+1]).
+int visible_end(const qi_req_host &r, int row) {
+  for (size_t b = 0; b + 1 < r.off.size(); ++b)
+    if (row < r.off[b + 1]) return (int)r.off[b + 1];
+  return r.n;
+}
+
+struct Unit {           // all row tiles of one (request, head): they read the same K/V
+  int req, head;
+  int64_t cost;         // key tiles processed, summed over the unit's row tiles
+  std::vector<int> tiles;
+};
+
+// Deal the (tile, head) items of a call to the XCDs: longest-processing-time-first over
+// units, so that the row tiles sharing a head's K/V stream run on one XCD and share its
+// L2, then interleave the per-XCD lists in launch order (workgroup i goes to XCD i % 8).
+void build_schedule(const qi_plan &p, const std::vector<qi_tile> &tiles,
+                    std::vector<int32_t> &sched) {
+  std::vector<Unit> units;
+  std::vector<std::vector<int>> by_req(p.n_req);
+  for (int i = 0; i < (int)tiles.size(); ++i) by_req[tiles[i].req].push_back(i);
+  for (int r = 0; r < p.n_req; ++r) {
+    if (by_req[r].empty()) continue;
+    std::vector<int> order = by_req[r];
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
+      return tiles[a].kend > tiles[b].kend;     // longest row tiles first
+    });
+    int64_t cost = 0;
+    for (int i : order) cost += (tiles[i].kend + QI_KERNEL_BN - 1) / QI_KERNEL_BN;
+    for (int h = 0; h < p.H; ++h) units.push_back(Unit{r, h, cost, order});
+  }
+  std::stable_sort(units.begin(), units.end(),
+                   [](const Unit &a, const Unit &b) { return a.cost > b.cost; });
+  std::vector<std::vector<int32_t>> bins(QI_NUM_XCD);
+  std::vector<int64_t> load(QI_NUM_XCD, 0);
+  for (const Unit &u : units) {
+    int best = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+    load[best] += u.cost;
+    for (int t : u.tiles) bins[best].push_back(t * p.H + u.head);
+  }
+  size_t len = 0;
+  for (auto &b : bins) len = std::max(len, b.size());
+  sched.assign(len * QI_NUM_XCD, -1);
+  for (size_t s = 0; s < len; ++s)
+    for (int x = 0; x < QI_NUM_XCD; ++x)
+      if (s < bins[x].size()) sched[s * QI_NUM_XCD + x] = bins[x][s];
+}
+
+void build_tiles(const qi_plan &p, int call, std::vector<qi_tile> &tiles) {
+  tiles.clear();
+  std::vector<std::pair<int, int>> blocks;
+  for (int r = 0; r < p.n_req; ++r) {
+    const qi_req_host &rq = p.req[r];
+    int nkeys = 0;
+    call_blocks(rq, call, blocks, nkeys);
+    for (auto [start, len] : blocks) {
+      for (int r0 = start; r0 < start + len; r0 += QI_KERNEL_BM) {
+        qi_tile t{};
+        t.nrows = std::min(QI_KERNEL_BM, start + len - r0);
+        t.kend = std::min(visible_end(rq, r0), nkeys);
+        t.req = r;
+        t.k_off = rq.k_off;
+        t.v_off = rq.v_off;
+        t.s_off = rq.s_off;
+        if (call == QI_CALL_PREFIX) {
+          t.q_tok = rq.pre_tok + r0;
+          t.kv_tok = rq.pre_tok;
+          t.lp = 0;
+        } else if (call == QI_CALL_DENOISE) {
+          t.q_tok = rq.img_tok + (r0 - rq.lp);
+          t.kv_tok = rq.img_tok;
+          t.lp = rq.lp;
+        } else {
+          t.q_tok = rq.all_tok + r0;
+          t.kv_tok = rq.all_tok;
+          t.lp = 0;
+        }
+        tiles.push_back(t);
+      }
+    }
+  }
+}
+
+template <typename T>
+void put(std::vector<uint8_t> &img, size_t off, const std::vector<T> &v) {
+  if (!v.empty()) std::memcpy(img.data() + off, v.data(), v.size() * sizeof(T));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *qi_status_string(qi_status st) {
+  switch (st) {
+    case QI_OK: return "ok";
+    case QI_ERR_INVALID_ARG: return "invalid argument";
+    case QI_ERR_UNSUPPORTED: return "unsupported configuration";
+    case QI_ERR_STATE: return "call out of order (workspace not uploaded or cache never built)";
+    case QI_ERR_BUFFER_TOO_SMALL: return "buffer too small";
+    case QI_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+qi_status qi_plan_create(const qi_wave_desc *d, qi_plan **out) {
+  if (!out) return QI_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (!d || !d->n_refs || !d->block_len) return QI_ERR_INVALID_ARG;
+  if (d->n_requests < 1 || d->n_requests > QI_MAX_REQUESTS) return QI_ERR_INVALID_ARG;
+  if (d->n_heads < 1 || d->n_heads > QI_MAX_HEADS) return QI_ERR_INVALID_ARG;
+  if (d->kv_dtype != QI_KV_BF16 && d->kv_dtype != QI_KV_FP8_E4M3) return QI_ERR_INVALID_ARG;
+  if (d->head_dim != 64 && d->head_dim != 128) return QI_ERR_UNSUPPORTED;
+
+  qi_plan *p = new (std::nothrow) qi_plan();
+  if (!p) return QI_ERR_INVALID_ARG;
+  p->n_req = d->n_requests;
+  p->H = d->n_heads;
+  p->D = d->head_dim;
+  p->kv = d->kv_dtype;
+  const int eb = p->kv == QI_KV_BF16 ? 2 : 1;
+
+  // requests, block offsets, packed token bases, cache layout
+  size_t pos = 0, cache_end = 0;
+  for (int r = 0; r < p->n_req; ++r) {
+    const int nr = d->n_refs[r];
+    if (nr < 0 || nr > QI_MAX_REFS) { delete p; return QI_ERR_INVALID_ARG; }
+    qi_req_host rq;
+    int64_t tot = 0;
+    rq.off.push_back(0);
+    for (int b = 0; b < nr + 2; ++b) {
+      const int32_t len = d->block_len[pos + b];
+      if (len <= 0) { delete p; return QI_ERR_INVALID_ARG; }
+      rq.bl.push_back(len);
+      tot += len;
+      if (tot >= (int64_t(1) << 24)) { delete p; return QI_ERR_INVALID_ARG; }
+      rq.off.push_back(tot);
+    }
+    pos += nr + 2;
+    rq.n = (int32_t)tot;
+    rq.nimg = rq.bl.back();
+    rq.lp = rq.n - rq.nimg;
+    rq.pre_tok = (int32_t)p->tot_pre;
+    rq.img_tok = (int32_t)p->tot_img;
+    rq.all_tok = (int32_t)p->tot_all;
+    p->tot_pre += rq.lp;
+    p->tot_img += rq.nimg;
+    p->tot_all += rq.n;
+    const size_t part = (size_t)p->H * rq.lp * p->D * eb;
+    rq.k_off = (int64_t)align_up(cache_end);
+    rq.v_off = (int64_t)align_up(rq.k_off + part);
+    rq.end = rq.v_off + (int64_t)part;
+    if (p->kv == QI_KV_FP8_E4M3) {
+      rq.s_off = (int64_t)align_up(rq.end);
+      rq.end = rq.s_off + 2 * 4 * p->H;
+    }
+    cache_end = (size_t)rq.end;
+    p->req.push_back(std::move(rq));
+  }
+  // every packed tensor must stay addressable with 32-bit element indices
+  if (p->tot_all * p->H * p->D >= (int64_t(1) << 31)) { delete p; return QI_ERR_INVALID_ARG; }
+  p->cache_bytes = align_up(cache_end);
+
+  // useful pairs: rows of block b see keys [0, off[b+1])
+  for (const qi_req_host &rq : p->req) {
+    const int nb = (int)rq.bl.size();
+    for (int b = 0; b < nb; ++b) {
+      const int64_t pr = (int64_t)rq.bl[b] * rq.off[b + 1];
+      p->pairs[QI_CALL_FULL] += pr;
+      if (b < nb - 1) p->pairs[QI_CALL_PREFIX] += pr;
+      else p->pairs[QI_CALL_DENOISE] += pr;
+    }
+  }
+
+  // device tables: per-request records, tiles and schedules of the three calls, partials
+  std::vector<qi_req_dev> reqs(p->n_req);
+  size_t nparts = 0;
+  for (int r = 0; r < p->n_req; ++r) {
+    const qi_req_host &rq = p->req[r];
+    qi_req_dev &e = reqs[r];
+    e.pre_tok = rq.pre_tok;
+    e.lp = rq.lp;
+    e.n_chunks = (rq.lp + QI_CACHE_CHUNK - 1) / QI_CACHE_CHUNK;
+    e.part_idx = (int32_t)nparts;
+    e.k_off = rq.k_off;
+    e.v_off = rq.v_off;
+    e.s_off = rq.s_off;
+    e.pad = 0;
+    nparts += (size_t)e.n_chunks * 2 * p->H;
+    p->max_chunks = std::max(p->max_chunks, e.n_chunks);
+  }
+  std::vector<qi_tile> tiles[3];
+  std::vector<int32_t> sched[3];
+  size_t off = 0;
+  p->reqs_off = off;
+  off = align_up(off + reqs.size() * sizeof(qi_req_dev));
+  for (int c = 0; c < 3; ++c) {
+    build_tiles(*p, c, tiles[c]);
+    build_schedule(*p, tiles[c], sched[c]);
+    p->n_tiles[c] = (int32_t)tiles[c].size();
+    p->sched_len[c] = (int32_t)sched[c].size();
+    p->tiles_off[c] = off;
+    off = align_up(off + tiles[c].size() * sizeof(qi_tile));
+    p->sched_off[c] = off;
+    off = align_up(off + sched[c].size() * sizeof(int32_t));
+  }
+  p->part_off = off;
+  p->part_floats = p->kv == QI_KV_FP8_E4M3 ? nparts : 0;
+  off = align_up(off + p->part_floats * sizeof(float));
+  p->ws_bytes = off;
+  p->ws_image.assign(p->part_off, 0);
+  put(p->ws_image, p->reqs_off, reqs);
+  for (int c = 0; c < 3; ++c) {
+    put(p->ws_image, p->tiles_off[c], tiles[c]);
+    put(p->ws_image, p->sched_off[c], sched[c]);
+  }
+  *out = p;
+  return QI_OK;
+}
+
+void qi_plan_destroy(qi_plan *p) { delete p; }
+
+qi_status qi_plan_sizes(const qi_plan *p, size_t *cache_bytes, size_t *workspace_bytes) {
+  if (!p) return QI_ERR_INVALID_ARG;
+  if (cache_bytes) *cache_bytes = p->cache_bytes;
+  if (workspace_bytes) *workspace_bytes = p->ws_bytes;
+  return QI_OK;
+}
+
+qi_status qi_plan_kernel_tile(const qi_plan *p, int32_t *bm, int32_t *bn) {
+  if (!p || !bm || !bn) return QI_ERR_INVALID_ARG;
+  *bm = QI_KERNEL_BM;
+  *bn = QI_KERNEL_BN;
+  return QI_OK;
+}
+
+qi_status qi_plan_tile_map(const qi_plan *p, int32_t call, int32_t bm, int32_t bn,
+                           uint8_t *host_out, size_t n, size_t *n_needed) {
+  if (!p || call < 0 || call > 2 || bm < 1 || bn < 1) return QI_ERR_INVALID_ARG;
+  std::vector<std::pair<int, int>> blocks;
+  size_t need = 0;
+  for (const qi_req_host &rq : p->req) {
+    int nkeys = 0;
+    call_blocks(rq, call, blocks, nkeys);
+    size_t rows = 0;
+    for (auto [start, len] : blocks) rows += (len + bm - 1) / bm;
+    need += rows * (size_t)((nkeys + bn - 1) / bn);
+  }
+  if (n_needed) *n_needed = need;
+  if (!host_out || n < need) return QI_ERR_BUFFER_TOO_SMALL;
+  size_t w = 0;
+  for (const qi_req_host &rq : p->req) {
+    int nkeys = 0;
+    call_blocks(rq, call, blocks, nkeys);
+    const int nkt = (nkeys + bn - 1) / bn;
+    for (auto [start, len] : blocks) {
+      const int vis = std::min(visible_end(rq, start), nkeys);
+      for (int r0 = start; r0 < start + len; r0 += bm) {
+        for (int j = 0; j < nkt; ++j) {
+          const int k0 = j * bn, k1 = std::min(nkeys, (j + 1) * bn);
+          host_out[w++] = k1 <= vis ? 2 : (k0 >= vis ? 0 : 1);
+        }
+      }
+    }
+  }
+  return QI_OK;
+}
+
+qi_status qi_plan_cache_offset(const qi_plan *p, int32_t req, int32_t kv, int32_t head,
+                               int32_t tok, size_t *byte_off) {
+  if (!p || !byte_off || req < 0 || req >= p->n_req || kv < 0 || kv > 2) return QI_ERR_INVALID_ARG;
+  const qi_req_host &rq = p->req[req];
+  if (kv == 2) {
+    if (p->kv != QI_KV_FP8_E4M3) return QI_ERR_INVALID_ARG;
+    *byte_off = (size_t)rq.s_off;
+    return QI_OK;
+  }
+  if (head < 0 || head >= p->H || tok < 0 || tok >= rq.lp) return QI_ERR_INVALID_ARG;
+  const size_t eb = p->kv == QI_KV_BF16 ? 2 : 1;
+  *byte_off = (size_t)(kv == 0 ? rq.k_off : rq.v_off) + ((size_t)head * rq.lp + tok) * p->D * eb;
+  return QI_OK;
+}
+
+qi_status qi_plan_pairs(const qi_plan *p, int32_t call, int64_t *pairs) {
+  if (!p || !pairs || call < 0 || call > 2) return QI_ERR_INVALID_ARG;
+  *pairs = p->pairs[call];
+  return QI_OK;
+}
+
+qi_status qi_plan_tokens(const qi_plan *p, int64_t *pre, int64_t *img, int64_t *all) {
+  if (!p) return QI_ERR_INVALID_ARG;
+  if (pre) *pre = p->tot_pre;
+  if (img) *img = p->tot_img;
+  if (all) *all = p->tot_all;
+  return QI_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,176 @@
+// Prefix KV cache write for step 0 (gfx950).
+//
+// The prompt and reference-image K/V computed at the first denoising step is stored and
+// reused by every later step of the same request, and rebuilt for the next request
+// (ThakiCloud blog "Qwen-Image-2.1 vLLM-Omni day 0", section "Serving architecture: the
+// cross-step prefix KV cache").  The cache may be kept in FP8 for long-prompt or
+// multi-image work (vLLM recipe "Qwen/Qwen-Image-2.1", section "Prefix KV cache").
+//
+// Source: packed token-major bf16 [sum L_p][H][D].  Destination, per request: K
+// [H][L_p][D], V [H][L_p][D], head-major so that each (request, head) key stream is one
+// contiguous run for the attention kernel's tile loads.
+//
+// bf16 cache: one pass, a re-layout copy (16 bytes per lane, coalesced reads and writes).
+// fp8 cache (OCP E4M3FN, one float32 scale per (request, head, K|V)):
+//   pass 1  every workgroup takes 64 tokens of one request and writes the max |x| per
+//           (K|V, head) of its tokens to the workspace (no atomics across workgroups:
+//           max is exact, so the result does not depend on any order);
+//   pass 2  every workgroup reduces its request's partials, derives scale = a/448 and
+//           inv = 448/a (correctly rounded float32 divisions; a == 0 gives 1 and 1), the
+//           first workgroup of the request stores the scales, and all quantise their
+//           tokens: code = nearest E4M3FN value to x*inv (float32 product), ties to the
+//           even code, saturating at 448.
+#include <hip/hip_runtime.h>
+
+#include "qi_internal.h"
+
+namespace {
+
+constexpr int NT = 256;
+constexpr int CHUNK = QI_CACHE_CHUNK;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float32 -> E4M3FN code: round to nearest, ties to even, saturate to +-448, keep the sign
+// of zero.  Integer arithmetic on the float32 bit pattern, exact for every input.
+__device__ __forceinline__ uint32_t e4m3fn_from_f32(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  uint32_t code;
+  if (a >= 0x43e00000u) {                 // |y| >= 448 (and inf): saturate
+    code = 0x7eu;
+  } else if (a < 0x3c800000u) {           // |y| < 2^-6: subnormal codes m * 2^-9
+    // |y| * 2^9 < 8 is exact in float32; rint rounds to nearest even; 8 encodes 2^-6
+    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  } else {                                // normal: keep 3 of the 23 mantissa bits
+    const uint32_t e = (a >> 23) - 127u + 7u;          // biased E4M3 exponent, 1..15
+    const uint32_t mant = a & 0x7fffffu;
+    const uint32_t keep = mant >> 20, rest = mant & 0xfffffu;
+    uint32_t c = (e << 3) | keep;
+    if (rest > 0x80000u || (rest == 0x80000u && (keep & 1u))) c += 1u;   // carry may bump e
+    code = c > 0x7eu ? 0x7eu : c;
+  }
+  return sign | code;
+}
+
+__global__ __launch_bounds__(NT) void cache_copy_bf16(const qi_req_dev *__restrict__ reqs,
+                                                      int H, int D,
+                                                      const uint4 *__restrict__ k_pre,
+                                                      const uint4 *__restrict__ v_pre,
+                                                      uint8_t *__restrict__ cache) {
+  const qi_req_dev r = reqs[blockIdx.y];
+  const int t0 = blockIdx.x * CHUNK;
+  if (t0 >= r.lp) return;
+  const int nt = min(CHUNK, r.lp - t0);
+  const int cpt = H * D / 8;   // 16-byte chunks per token
+  for (int i = threadIdx.x; i < nt * cpt; i += NT) {
+    const int tok = t0 + i / cpt, rem = i % cpt;
+    const int h = rem / (D / 8), c = rem % (D / 8);
+    const int64_t src = (int64_t)(r.pre_tok + tok) * cpt + rem;
+    const int64_t dst = ((int64_t)h * r.lp + tok) * D * 2 + c * 16;
+    *reinterpret_cast<uint4 *>(cache + r.k_off + dst) = k_pre[src];
+    *reinterpret_cast<uint4 *>(cache + r.v_off + dst) = v_pre[src];
+  }
+}
+
+__global__ __launch_bounds__(NT) void cache_absmax_fp8(const qi_req_dev *__restrict__ reqs,
+                                                       int H, int D,
+                                                       const uint4 *__restrict__ k_pre,
+                                                       const uint4 *__restrict__ v_pre,
+                                                       float *__restrict__ partials) {
+  extern __shared__ unsigned int smax[];   // [2][H], float bits of non-negative maxima
+  const qi_req_dev r = reqs[blockIdx.y];
+  const int t0 = blockIdx.x * CHUNK;
+  if (t0 >= r.lp) return;
+  for (int i = threadIdx.x; i < 2 * H; i += NT) smax[i] = 0u;
+  __syncthreads();
+  const int nt = min(CHUNK, r.lp - t0);
+  const int cpt = H * D / 8;
+  for (int i = threadIdx.x; i < nt * cpt; i += NT) {
+    const int tok = t0 + i / cpt, rem = i % cpt;
+    const int h = rem / (D / 8);
+    const int64_t src = (int64_t)(r.pre_tok + tok) * cpt + rem;
+    const uint4 kv[2] = {k_pre[src], v_pre[src]};
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const uint32_t x[4] = {kv[w].x, kv[w].y, kv[w].z, kv[w].w};
+      float m = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) m = fmaxf(m, fmaxf(fabsf(bf16_lo(x[j])), fabsf(bf16_hi(x[j]))));
+      atomicMax(&smax[w * H + h], __float_as_uint(m));   // LDS atomic; order-free
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 2 * H; i += NT)
+    partials[r.part_idx + blockIdx.x * 2 * H + i] = __uint_as_float(smax[i]);
+}
+
+__global__ __launch_bounds__(NT) void cache_quant_fp8(const qi_req_dev *__restrict__ reqs,
+                                                      int H, int D,
+                                                      const uint4 *__restrict__ k_pre,
+                                                      const uint4 *__restrict__ v_pre,
+                                                      const float *__restrict__ partials,
+                                                      uint8_t *__restrict__ cache) {
+  extern __shared__ float sinv[];   // [2][H] reciprocal scales
+  const qi_req_dev r = reqs[blockIdx.y];
+  const int t0 = blockIdx.x * CHUNK;
+  if (t0 >= r.lp) return;
+  for (int i = threadIdx.x; i < 2 * H; i += NT) {
+    float a = 0.0f;
+    for (int c = 0; c < r.n_chunks; ++c) a = fmaxf(a, partials[r.part_idx + c * 2 * H + i]);
+    const float scale = a > 0.0f ? __fdiv_rn(a, 448.0f) : 1.0f;
+    sinv[i] = a > 0.0f ? __fdiv_rn(448.0f, a) : 1.0f;
+    if (blockIdx.x == 0) reinterpret_cast<float *>(cache + r.s_off)[i] = scale;
+  }
+  __syncthreads();
+  const int nt = min(CHUNK, r.lp - t0);
+  const int cpt = H * D / 8;
+  for (int i = threadIdx.x; i < nt * cpt; i += NT) {
+    const int tok = t0 + i / cpt, rem = i % cpt;
+    const int h = rem / (D / 8), c = rem % (D / 8);
+    const int64_t src = (int64_t)(r.pre_tok + tok) * cpt + rem;
+    const int64_t dst = ((int64_t)h * r.lp + tok) * D + c * 8;
+    const uint4 kv[2] = {k_pre[src], v_pre[src]};
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const float inv = sinv[w * H + h];
+      const uint32_t x[4] = {kv[w].x, kv[w].y, kv[w].z, kv[w].w};
+      uint32_t out[2] = {0u, 0u};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t lo = e4m3fn_from_f32(bf16_lo(x[j]) * inv);
+        const uint32_t hi = e4m3fn_from_f32(bf16_hi(x[j]) * inv);
+        out[j >> 1] |= (lo | (hi << 8)) << (16 * (j & 1));
+      }
+      *reinterpret_cast<uint2 *>(cache + (w == 0 ? r.k_off : r.v_off) + dst) =
+          make_uint2(out[0], out[1]);
+    }
+  }
+}
+
+}  // namespace
+
+qi_status qi_launch_cache_write(const qi_plan *p, const void *k_pre, const void *v_pre,
+                                void *cache, void *stream) {
+  if (p->max_chunks == 0) return QI_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t *ws = static_cast<uint8_t *>(p->d_ws);
+  const qi_req_dev *reqs = reinterpret_cast<const qi_req_dev *>(ws + p->reqs_off);
+  const dim3 grid(p->max_chunks, p->n_req);
+  const uint4 *k = static_cast<const uint4 *>(k_pre);
+  const uint4 *v = static_cast<const uint4 *>(v_pre);
+  uint8_t *c = static_cast<uint8_t *>(cache);
+  if (p->kv == QI_KV_BF16) {
+    hipLaunchKernelGGL(cache_copy_bf16, grid, dim3(NT), 0, s, reqs, p->H, p->D, k, v, c);
+  } else {
+    float *part = reinterpret_cast<float *>(ws + p->part_off);
+    const size_t sh = 2 * p->H * sizeof(float);
+    hipLaunchKernelGGL(cache_absmax_fp8, grid, dim3(NT), sh, s, reqs, p->H, p->D, k, v, part);
+    if (hipGetLastError() != hipSuccess) return QI_ERR_HIP;
+    hipLaunchKernelGGL(cache_quant_fp8, grid, dim3(NT), sh, s, reqs, p->H, p->D, k, v,
+                       (const float *)part, c);
+  }
+  return hipGetLastError() == hipSuccess ? QI_OK : QI_ERR_HIP;
+}

@@ -1,0 +1,76 @@
+// Internal declarations shared by the host plan (plan.cpp), the C-ABI entry points
+// (api.hip) and the kernels (attn_fwd.hip, prefix_kv.hip).  Not part of the ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "../../include/qi.h"
+
+// Attention tile: rows per workgroup (4 wavefronts x 32 query rows) x keys per step.
+#define QI_KERNEL_BM 128
+#define QI_KERNEL_BN 64
+// Number of XCDs of the MI355X; workgroups are dealt to them round-robin in launch order.
+#define QI_NUM_XCD 8
+// Prefix tokens per workgroup in the cache-write kernels.
+#define QI_CACHE_CHUNK 64
+
+// One row tile of one request for one call (device table entry, 48 bytes).
+struct qi_tile {
+  int32_t q_tok;      // packed token index (in the call's Q and O tensors) of the first row
+  int32_t nrows;      // 1 .. QI_KERNEL_BM
+  int32_t kend;       // attended keys are positions [0, kend) of the request
+  int32_t kv_tok;     // packed token index (in the call's live K/V) of key position `lp`
+  int32_t lp;         // keys below lp come from the prefix cache (denoise); else 0
+  int32_t req;        // request index
+  int64_t k_off;      // byte offset of the request's cached K  [H][lp][D]   (denoise)
+  int64_t v_off;      // byte offset of the request's cached V  [H][lp][D]   (denoise)
+  int64_t s_off;      // byte offset of the request's scales [2][H] float32 (fp8 denoise)
+};
+static_assert(sizeof(qi_tile) == 48, "qi_tile is a 48-byte device record");
+
+// Per-request record for the cache-write kernels (device table entry, 48 bytes).
+struct qi_req_dev {
+  int32_t pre_tok;    // packed token index of the request's first prefix token
+  int32_t lp;         // prefix length
+  int32_t n_chunks;   // ceil(lp / QI_CACHE_CHUNK)
+  int32_t part_idx;   // first float of the request's absmax partials [n_chunks][2][H]
+  int64_t k_off, v_off, s_off;
+  int64_t pad;
+};
+static_assert(sizeof(qi_req_dev) == 48, "qi_req_dev is a 48-byte device record");
+
+struct qi_req_host {
+  std::vector<int32_t> bl;    // text, ref_1..ref_R, image
+  std::vector<int64_t> off;   // block offsets, size bl.size() + 1
+  int32_t lp = 0, nimg = 0, n = 0;
+  int32_t pre_tok = 0, img_tok = 0, all_tok = 0;
+  int64_t k_off = 0, v_off = 0, s_off = -1, end = 0;
+};
+
+struct qi_plan {
+  int32_t n_req = 0, H = 0, D = 0, kv = 0;
+  std::vector<qi_req_host> req;
+  int64_t tot_pre = 0, tot_img = 0, tot_all = 0;
+  size_t cache_bytes = 0;
+  int64_t pairs[3] = {0, 0, 0};
+
+  // device tables, all inside one workspace image (host copy kept for upload)
+  std::vector<uint8_t> ws_image;
+  size_t ws_bytes = 0;
+  size_t tiles_off[3] = {0, 0, 0}, sched_off[3] = {0, 0, 0};
+  int32_t n_tiles[3] = {0, 0, 0}, sched_len[3] = {0, 0, 0};
+  size_t reqs_off = 0, part_off = 0, part_floats = 0;
+  int32_t max_chunks = 0;
+
+  void *d_ws = nullptr;   // caller's workspace once uploaded
+  bool built = false;     // a prefix build has been enqueued on this plan
+};
+
+// Kernel launchers (defined in the .hip files).  Return QI_OK or QI_ERR_HIP.
+qi_status qi_launch_attention(const qi_plan *p, int call, const void *q, const void *k,
+                              const void *v, void *o, const void *cache, void *stream);
+qi_status qi_launch_cache_write(const qi_plan *p, const void *k_pre, const void *v_pre,
+                                void *cache, void *stream);

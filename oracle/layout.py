@@ -66,6 +66,47 @@ def cache_offset(regions, head_dim, kv_dtype, req, kv, head, tok):
     return base + (head * reg["lp"] + tok) * head_dim * eb
 
 
+def bf16_bits(values):
+    """uint16 bit patterns of values that are exactly representable in bf16."""
+    f32 = np.ascontiguousarray(values, dtype=np.float32)
+    if not np.array_equal(f32.astype(np.float64), np.asarray(values, dtype=np.float64)):
+        raise ValueError("values are not bf16-exact")
+    bits = f32.view(np.uint32)
+    if np.any(bits & 0xFFFF):
+        raise ValueError("values are not bf16-exact")
+    return (bits >> 16).astype(np.uint16)
+
+
+def cache_image(requests, n_heads, head_dim, kv_dtype, k_pre, v_pre):
+    """Expected bytes of the cache arena after the prefix build.
+
+    k_pre / v_pre: packed token-major [sum L_p, H, D] bf16-exact values of the wave.
+    Returns (image uint8 [total], defined bool [total]); padding bytes are undefined.
+    """
+    from . import fp8 as F
+    regions, total = cache_layout(requests, n_heads, head_dim, kv_dtype)
+    img = np.zeros(total, dtype=np.uint8)
+    defined = np.zeros(total, dtype=bool)
+    tok = 0
+    for reg in regions:
+        lp = reg["lp"]
+        kr = np.asarray(k_pre[tok:tok + lp], dtype=np.float64)
+        vr = np.asarray(v_pre[tok:tok + lp], dtype=np.float64)
+        tok += lp
+        if kv_dtype == KV_BF16:
+            parts = [(reg["k_off"], bf16_bits(np.transpose(kr, (1, 0, 2))).view(np.uint8)),
+                     (reg["v_off"], bf16_bits(np.transpose(vr, (1, 0, 2))).view(np.uint8))]
+        else:
+            ck, cv, sc = F.quantize_prefix(kr, vr)
+            parts = [(reg["k_off"], ck), (reg["v_off"], cv),
+                     (reg["s_off"], sc.astype("<f4").view(np.uint8))]
+        for off, arr in parts:
+            flat = np.ascontiguousarray(arr).reshape(-1).view(np.uint8)
+            img[off:off + flat.size] = flat
+            defined[off:off + flat.size] = True
+    return img, defined
+
+
 def call_rows_keys(block_len, call):
     """(row blocks, key count) of one request for a call.  Row blocks are (start, len)."""
     off = block_offsets(block_len)

@@ -1,0 +1,148 @@
+"""Shared helpers of the GPU tests: run a wave through libqi (C ABI via the ctypes
+binding) and evaluate the same wave with the fp64 oracle."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+from block_causal_attention_qi_amd import qi, synth
+from oracle import attention as A
+from oracle import fp8 as F
+from oracle import layout as L
+
+BF16_MAXABS, BF16_RELRMS = 2e-2, 5e-3     # bf16 path bar
+FP8_MAXABS, FP8_RELRMS = 8e-2, 2e-2       # fp8 prefix-cache path bar
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def errors(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert np.all(np.isfinite(got)), "non-finite output"
+    d = got - ref
+    return float(np.max(np.abs(d))), float(np.linalg.norm(d) / np.linalg.norm(ref))
+
+
+def check(got, ref, maxabs, relrms, what):
+    ma, rr = errors(got, ref)
+    say("  %-40s max-abs %.3e  rel-RMS %.3e" % (what, ma, rr))
+    assert ma <= maxabs and rr <= relrms, (what, ma, rr)
+    return ma, rr
+
+
+def nan_like(shape, device):
+    return torch.full(shape, float("nan"), dtype=torch.bfloat16, device=device)
+
+
+class GpuWave:
+    """Device copies of a wave's inputs plus a plan, cache and workspace."""
+
+    def __init__(self, x: synth.WaveInputs, device, steps=1, kv=None):
+        w = x.workload
+        self.x, self.w, self.dev = x, w, device
+        self.kv = kv or w.kv_dtype
+        self.plan = qi.Plan(w.requests, w.n_heads, w.head_dim, self.kv)
+        self.cache, self.ws = qi.allocate(self.plan, device)
+        b = lambda a: synth.to_bf16(a, device)
+        self.q_pre, self.k_pre, self.v_pre = b(x.q_pre), b(x.k_pre), b(x.v_pre)
+        self.img = [(b(x.q_img[s]), b(x.k_img[s]), b(x.v_img[s])) for s in range(steps)]
+        self.full_in = {}
+
+    def build(self):
+        o = nan_like(tuple(self.q_pre.shape), self.dev)
+        qi.qi_prefix_kv_build(self.plan, self.q_pre, self.k_pre, self.v_pre, o, self.cache)
+        return o
+
+    def denoise(self, step=0):
+        q, k, v = self.img[step]
+        o = nan_like(tuple(q.shape), self.dev)
+        qi.qi_denoise_attn_step(self.plan, self.cache, q, k, v, o)
+        return o
+
+    def full(self, step=0):
+        if step not in self.full_in:
+            self.full_in[step] = [synth.to_bf16(t, self.dev) for t in self.x.full(step)]
+        q, k, v = self.full_in[step]
+        o = nan_like(tuple(q.shape), self.dev)
+        qi.qi_attn_full_reference_step(self.plan, q, k, v, o)
+        return o
+
+
+def f64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def exact_inputs(x: synth.WaveInputs, step=0):
+    """bf16-exact float64 views of a wave's inputs (what the GPU reads)."""
+    return dict(q_pre=synth.bf16_exact(x.q_pre), k_pre=synth.bf16_exact(x.k_pre),
+                v_pre=synth.bf16_exact(x.v_pre), q_img=synth.bf16_exact(x.q_img[step]),
+                k_img=synth.bf16_exact(x.k_img[step]), v_img=synth.bf16_exact(x.v_img[step]))
+
+
+def split(w, arr, which):
+    """Per-request slices of a packed array; which in ('pre', 'img', 'all')."""
+    lens = {"pre": w.prefix_lens, "img": w.image_lens, "all": w.total_lens}[which]
+    out, o = [], 0
+    for n in lens:
+        out.append(arr[o:o + n])
+        o += n
+    return out
+
+
+def oracle_prefix_values(w, e, kv):
+    """Per request: the prefix K/V the denoising step reads (bf16 values, or the
+    dequantised fp8 cache)."""
+    ks, vs = split(w, e["k_pre"], "pre"), split(w, e["v_pre"], "pre")
+    if kv == "bf16":
+        return ks, vs
+    out_k, out_v = [], []
+    for k, v in zip(ks, vs):
+        ck, cv, sc = F.quantize_prefix(k, v)
+        out_k.append(F.dequantize(ck, sc[0]))
+        out_v.append(F.dequantize(cv, sc[1]))
+    return out_k, out_v
+
+
+def oracle_rows(w, call, e, rows_per_req, kv="bf16", heads=None):
+    """Oracle output for selected rows (call-relative indices per request) and heads.
+    Returns list per request of [len(rows), len(heads), D]."""
+    heads = list(range(w.n_heads)) if heads is None else list(heads)
+    kp, vp = oracle_prefix_values(w, e, kv) if call == L.CALL_DENOISE else (None, None)
+    res = []
+    for r, bl in enumerate(w.requests):
+        rows = np.asarray(rows_per_req[r], dtype=np.int64)
+        lp, n = sum(bl[:-1]), sum(bl)
+        if call == L.CALL_PREFIX:
+            q = split(w, e["q_pre"], "pre")[r]
+            k, v = split(w, e["k_pre"], "pre")[r], split(w, e["v_pre"], "pre")[r]
+            mask = A.allowed_mask(bl[:-1], rows=rows)
+        elif call == L.CALL_DENOISE:
+            q = split(w, e["q_img"], "img")[r]
+            k = np.concatenate([kp[r], split(w, e["k_img"], "img")[r]])
+            v = np.concatenate([vp[r], split(w, e["v_img"], "img")[r]])
+            mask = A.allowed_mask(bl, rows=rows + lp)
+        else:
+            q = np.concatenate([split(w, e["q_pre"], "pre")[r], split(w, e["q_img"], "img")[r]])
+            k = np.concatenate([split(w, e["k_pre"], "pre")[r], split(w, e["k_img"], "img")[r]])
+            v = np.concatenate([split(w, e["v_pre"], "pre")[r], split(w, e["v_img"], "img")[r]])
+            mask = A.allowed_mask(bl, rows=rows)
+        res.append(A.masked_attention(q[rows][:, heads], k[:, heads], v[:, heads], mask))
+    return res
+
+
+def sample_rows(bl, call, bm, rng, n_random):
+    """Call-relative rows: first/last rows of every block and row tile, plus random rows."""
+    lp = sum(bl[:-1])
+    tiles = L.row_tiles(bl, call, bm)
+    base = lp if call == L.CALL_DENOISE else 0
+    rows = set()
+    for r0, nr in tiles:
+        rows.update({r0 - base, r0 + nr - 1 - base, r0 + min(nr - 1, 31) - base})
+    total = sum(nr for _, nr in tiles)
+    rows.update(int(x) for x in rng.integers(0, total, n_random))
+    return sorted(rows)

@@ -137,3 +137,47 @@ def test_four_reference_recompute_fraction(facts):
     fr = facts["four_reference_recompute_fraction"]
     bl = synth.WORKLOADS["edit4"].requests[0]
     assert abs(bl[-1] / sum(bl) - fr["value"]) <= fr["tolerance"]
+
+
+def test_cache_image_reads_back_through_offsets():
+    """Bytes at cache_offset(...) hold torch's bf16 bits of K/V (bf16 cache), or torch's
+    E4M3FN cast of x*inv with float32 scales absmax/448 (fp8 cache)."""
+    import torch
+    rng = np.random.default_rng(21)
+    reqs = [[3, 5, 4], [2, 6], [7, 1, 2, 9]]
+    h, d = 2, 64
+    lp = sum(sum(b[:-1]) for b in reqs)
+    kf = torch.from_numpy(rng.standard_normal((lp, h, d)).astype(np.float32)).to(torch.bfloat16)
+    vf = torch.from_numpy(rng.standard_normal((lp, h, d)).astype(np.float32) * 2).to(torch.bfloat16)
+    k64, v64 = kf.double().numpy(), vf.double().numpy()
+    for kv_dtype in (L.KV_BF16, L.KV_FP8):
+        img, defined = L.cache_image(reqs, h, d, kv_dtype, k64, v64)
+        regs, total = L.cache_layout(reqs, h, d, kv_dtype)
+        assert img.size == total
+        tok0 = 0
+        for r, bl in enumerate(reqs):
+            n = sum(bl[:-1])
+            for which, src in ((0, kf), (1, vf)):
+                x = src[tok0:tok0 + n]                       # [n, h, d]
+                if kv_dtype == L.KV_FP8:
+                    s_off = regs[r]["s_off"]
+                    scales = img[s_off:s_off + 8 * h].view("<f4").reshape(2, h)
+                for hh in range(h):
+                    for t in range(n):
+                        off = L.cache_offset(regs, d, kv_dtype, r, which, hh, t)
+                        if kv_dtype == L.KV_BF16:
+                            want = x[t, hh].view(torch.int16).numpy().view(np.uint8)
+                            got = img[off:off + 2 * d]
+                        else:
+                            a = np.float32(x[:, hh].float().abs().max().item())
+                            assert scales[which, hh] == a / np.float32(448)
+                            y = x[t, hh].float() * torch.tensor(np.float32(448) / a)
+                            want = y.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+                            got = img[off:off + d]
+                        assert np.array_equal(got, want)
+                        assert defined[off:off + got.size].all()
+            tok0 += n
+        # everything defined is accounted for by K, V (and scales)
+        eb = 2 if kv_dtype == L.KV_BF16 else 1
+        extra = 8 * h * len(reqs) if kv_dtype == L.KV_FP8 else 0
+        assert defined.sum() == 2 * lp * h * d * eb + extra
