@@ -1,6 +1,6 @@
 // Block-causal attention forward for gfx950 (CDNA4), bf16 MFMA, fp32 online softmax.
 //
-// One workgroup (4 wavefronts, 256 lanes) owns one (request, head, row tile of <= 128
+// One workgroup (8 wavefronts, 512 lanes) owns one (request, head, row tile of <= 256
 // rows); each wavefront owns 32 query rows and keeps its Q fragments and its O
 // accumulator in registers for the whole key loop.  Row tiles never cross a block, so
 // every row of a tile sees the same key prefix [0, kend) (block-causal rule: a row of
@@ -25,11 +25,22 @@
 //   running max m is only raised when a row's tile max exceeds it by more than 8 (then
 //   every row of the wavefront is rescaled exactly); otherwise p <= 2^8, which bf16 and
 //   fp32 hold without loss of relative precision.  The result is the same softmax.
-//   O^T += V^T P^T   16 x MFMA (A = V^T from LDS, B = P packed to bf16 in VGPRs); the
-//   key order inside each 16-key MFMA step is permuted consistently on both operands so
-//   that P never leaves the lane that computed it.
-// LDS: K tile [64 keys][D] and V^T tile [D][64 keys], bf16, XOR-swizzled in 16-byte
-// chunks, double-buffered; the next tile is prefetched into registers during compute.
+//   O^T += V^T P^T   16 x MFMA (A = V^T, read from the natural [key][dim] V tile with
+//   the gfx950 LDS transpose read ds_read_b64_tr_b16; B = P packed to bf16 in VGPRs);
+//   the key order inside each 16-key MFMA step is permuted consistently on both
+//   operands so that P never leaves the lane that computed it.
+// LDS: K and V tiles [64 keys][D] bf16, XOR-swizzled in 16-byte chunks so that every LDS
+// access of the kernel is free of bank conflicts on the 64-bank gfx950 LDS (16 lanes per
+// cycle for 16-byte reads, 32 lanes per cycle for 8-byte reads).
+//
+// Workgroup: 8 wavefronts (two per SIMD) own 256 query rows; they form two groups of four
+// that alternate phases ("ping-pong"): while one group runs its MFMA phase (QK^T of key
+// tile j and PV of tile j-1) the other runs its VALU phase (softmax of its tile), and the
+// two swap at every workgroup barrier, so each SIMD always has one wavefront feeding the
+// matrix core and one feeding the vector ALU.  The MFMA-phase wavefront raises its issue
+// priority.  bf16 tiles go straight from global memory into LDS (global_load_lds_dwordx4,
+// no staging registers), double-buffered, one tile ahead.  The fp8 cache is staged
+// through registers, where its codes are dequantised, with a plain loop.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -39,31 +50,54 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int BM = QI_KERNEL_BM;
 constexpr int BN = QI_KERNEL_BN;
-constexpr int NT = 256;
+constexpr int NT = 512;                 // 8 wavefronts
+constexpr int NWAVE = NT / 64;
 constexpr float TAU = 8.0f;   // lazy-rescale threshold, log2 units
 
 enum { SRC_ONE = 0, SRC_CACHE_BF16 = 1, SRC_CACHE_FP8 = 2 };
 
 template <int D>
 struct Cfg {
-  static constexpr int CH = D / 8;           // 16-byte chunks per K row
-  static constexpr int KROWS = NT / CH;      // K rows staged per pass
-  static constexpr int KPASS = BN / KROWS;   // passes per K tile
-  static constexpr int KPT = BN * CH / NT;   // consecutive keys per lane in V staging
+  static constexpr int CH = D / 8;           // 16-byte chunks per K/V row
+  static constexpr int ROWS = NT / CH;       // rows staged per pass (all 256 lanes)
+  static constexpr int PASS = BN / ROWS;     // passes per tile
   static constexpr int QS = D / 16;          // MFMA k-steps over the head dim
   static constexpr int DB = D / 32;          // 32-wide blocks of the output
   static constexpr int TILE = BN * D;        // bf16 elements per staged K (or V) tile
-  static_assert(KPASS * KROWS == BN && (KPT == 2 || KPT == 4), "tile shape");
+  static constexpr int IPW = D / 64;         // 1 KiB direct loads per wavefront per tile
+  static constexpr int RPK = 512 / D;        // rows per 1 KiB
+  static_assert(PASS * ROWS == BN && IPW * RPK * NWAVE == BN, "tile shape");
+  // Physical 16-byte chunk = logical chunk ^ swz(row).  One swizzle serves both tiles:
+  //  K reads: 16 lanes read one chunk of 16 consecutive rows -> 16 distinct bank groups;
+  //  V transpose reads: 32 lanes read 64 bytes of 4 consecutive rows -> 64 distinct banks.
+  __device__ static constexpr int swz(int r) {
+    return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+  }
 };
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   bf16x2_t v = {(__bf16)a, (__bf16)b};   // round to nearest even (v_cvt_pk_bf16_f32)
   return __builtin_bit_cast(uint32_t, v);
+}
+
+// max over the two lanes (j, j + 32) holding one query row
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // 8 E4M3FN codes -> 8 bf16 of code * scale (value * scale in fp32, rounded once to bf16)
@@ -80,16 +114,6 @@ __device__ __forceinline__ uint4 dequant8(uint32_t lo, uint32_t hi, float scale)
   return r;
 }
 
-__device__ __forceinline__ uint32_t word(const uint4 &v, int j) {
-  return j == 0 ? v.x : (j == 1 ? v.y : (j == 2 ? v.z : v.w));
-}
-
-// Physical position of key k inside a V^T row: bits 2 and 3 swapped, so that the 8 keys
-// one lane feeds to a 16-key PV step are contiguous.
-__device__ __forceinline__ int vpos(int k) {
-  return (k & ~0xC) | ((k & 4) << 1) | ((k & 8) >> 1);
-}
-
 struct TileArgs {
   const __bf16 *k, *v;       // live K/V (token-major [tokens][H][D])
   const uint8_t *cache;      // prefix cache arena (denoise) or null
@@ -98,90 +122,175 @@ struct TileArgs {
   float k_scale, v_scale;    // fp8 dequantisation scales of this (request, head)
 };
 
+// Where a key tile comes from: wholly from the live tensor, wholly from the cache, or
+// mixed / partly past kend (per-row choice).
+enum { LIVE = 0, CACHED = 1, MIXED = 2 };
+template <int SRC>
+__device__ __forceinline__ int tile_kind(int kt, const TileArgs &a) {
+  const int k0 = kt * BN, k1 = k0 + BN;
+  if (k1 > a.kend) return MIXED;
+  if (SRC == SRC_ONE || k0 >= a.lp) return LIVE;
+  return k1 <= a.lp ? CACHED : MIXED;
+}
+
+// ---------------------------------------------------------------------------------------
+// Direct global -> LDS tile loads (bf16 sources).  Instruction i of wavefront w fills the
+// i-th KiB of the wavefront's share of a tile: lane l writes the 16 bytes at KiB offset
+// 16 l, i.e. row (w * IPW + i) * RPK + l / CH, physical chunk l % CH, so it loads logical
+// chunk (l % CH) ^ swz(row) of that key row.
+template <int D, int SRC>
+struct Direct {
+  using C = Cfg<D>;
+  int live_off[C::IPW];    // element offsets inside the live tensor, from the tile's key 0
+  int cache_off[C::IPW];   // element offsets inside one cached head, from the tile's key 0
+
+  __device__ __forceinline__ static int row_of(int i) {
+    return ((threadIdx.x >> 6) * C::IPW + i) * C::RPK + (threadIdx.x & 63) / C::CH;
+  }
+  __device__ __forceinline__ static int chunk_of(int i) {
+    return ((threadIdx.x & 63) % C::CH) ^ C::swz(row_of(i));
+  }
+
+  __device__ __forceinline__ void init(const TileArgs &a) {
+#pragma unroll
+    for (int i = 0; i < C::IPW; ++i) {
+      live_off[i] = row_of(i) * a.H * D + chunk_of(i) * 8;
+      cache_off[i] = row_of(i) * D + chunk_of(i) * 8;
+    }
+  }
+
+  __device__ __forceinline__ static void dma(const __bf16 *src, __bf16 *tile, int i) {
+    __bf16 *dst = tile + ((threadIdx.x >> 6) * C::IPW + i) * 512;   // wavefront-uniform
+    __builtin_amdgcn_global_load_lds(src, (lds_void_t *)dst, 16, 0, 0);
+  }
+
+  // issue the loads of tile kt of one tensor (K: live = a.k, coff = a.k_off)
+  __device__ __forceinline__ void issue(int kt, const TileArgs &a, const __bf16 *live,
+                                        int64_t coff, __bf16 *tile) const {
+    const int k0 = kt * BN;
+    const int kd = tile_kind<SRC>(kt, a);
+    if (kd == LIVE) {
+      const __bf16 *base = live + ((int64_t)(a.kv_tok + k0 - a.lp) * a.H + a.h) * D;
+#pragma unroll
+      for (int i = 0; i < C::IPW; ++i) dma(base + live_off[i], tile, i);
+    } else if (SRC != SRC_ONE && kd == CACHED) {
+      const __bf16 *base =
+          reinterpret_cast<const __bf16 *>(a.cache + coff) + (int64_t)(a.h * a.lp + k0) * D;
+#pragma unroll
+      for (int i = 0; i < C::IPW; ++i) dma(base + cache_off[i], tile, i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::IPW; ++i) {
+        // keys past kend load key kend - 1: finite values of this request, masked later
+        const int key = min(k0 + row_of(i), a.kend - 1);
+        const __bf16 *src;
+        if (SRC != SRC_ONE && key < a.lp)
+          src = reinterpret_cast<const __bf16 *>(a.cache + coff) + (int64_t)(a.h * a.lp + key) * D;
+        else
+          src = live + ((int64_t)(a.kv_tok + key - a.lp) * a.H + a.h) * D;
+        dma(src + chunk_of(i) * 8, tile, i);
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------------------
+// Register-staged tile loads (fp8 cache): lane t stages chunk t % CH of rows
+// t / CH + i * ROWS (i < PASS) of both tiles and dequantises cached rows on the way.
 template <int D, int SRC>
 struct Stage {
-  uint4 kr[Cfg<D>::KPASS];
-  uint4 vr[Cfg<D>::KPT];
+  using C = Cfg<D>;
+  uint4 kr[C::PASS];
+  uint4 vr[C::PASS];
+  int row0, chunk;
+  int live_off[C::PASS];
+  int cache_off[C::PASS];
 
-  __device__ __forceinline__ static uint4 fetch(const __bf16 *live, int64_t coff, int key,
-                                                int chunk, const TileArgs &a) {
+  __device__ __forceinline__ void init(const TileArgs &a) {
+    row0 = threadIdx.x / C::CH;
+    chunk = threadIdx.x % C::CH;
+#pragma unroll
+    for (int i = 0; i < C::PASS; ++i) {
+      const int r = row0 + i * C::ROWS;
+      live_off[i] = r * a.H * D + chunk * 8;
+      cache_off[i] = r * D + chunk * 8;
+    }
+  }
+
+  __device__ __forceinline__ uint4 fetch_row(const __bf16 *live, int64_t coff, int key,
+                                             const TileArgs &a) const {
     if (key >= a.kend) return make_uint4(0, 0, 0, 0);
     if (SRC != SRC_ONE && key < a.lp) {
-      if (SRC == SRC_CACHE_BF16) {
-        const uint8_t *p = a.cache + coff + ((int64_t)(a.h * a.lp + key) * D + chunk * 8) * 2;
-        return *reinterpret_cast<const uint4 *>(p);
-      } else {
-        const uint8_t *p = a.cache + coff + (int64_t)(a.h * a.lp + key) * D + chunk * 8;
-        const uint2 raw = *reinterpret_cast<const uint2 *>(p);
-        return make_uint4(raw.x, raw.y, 0, 0);
-      }
+      const uint8_t *p = a.cache + coff + (int64_t)(a.h * a.lp + key) * D + chunk * 8;
+      const uint2 raw = *reinterpret_cast<const uint2 *>(p);
+      return make_uint4(raw.x, raw.y, 0, 0);
     }
     const __bf16 *p = live + ((int64_t)(a.kv_tok + key - a.lp) * a.H + a.h) * D + chunk * 8;
     return *reinterpret_cast<const uint4 *>(p);
   }
 
   __device__ __forceinline__ void load(int kt, const TileArgs &a) {
-    using C = Cfg<D>;
-    const int t = threadIdx.x;
-    const int kc = t % C::CH, kr0 = t / C::CH;
+    const int k0 = kt * BN;
+    const int kd = tile_kind<SRC>(kt, a);
+    if (kd == LIVE) {
+      const int64_t base = ((int64_t)(a.kv_tok + k0 - a.lp) * a.H + a.h) * D;
+      const __bf16 *kb = a.k + base, *vb = a.v + base;
 #pragma unroll
-    for (int i = 0; i < C::KPASS; ++i)
-      kr[i] = fetch(a.k, a.k_off, kt * BN + kr0 + i * C::KROWS, kc, a);
-    const int dg = t % C::CH, kg = t / C::CH;
+      for (int i = 0; i < C::PASS; ++i) {
+        kr[i] = *reinterpret_cast<const uint4 *>(kb + live_off[i]);
+        vr[i] = *reinterpret_cast<const uint4 *>(vb + live_off[i]);
+      }
+    } else if (kd == CACHED) {
+      const int64_t e0 = (int64_t)(a.h * a.lp + k0) * D;
+      const uint8_t *kb = a.cache + a.k_off + e0, *vb = a.cache + a.v_off + e0;
 #pragma unroll
-    for (int i = 0; i < C::KPT; ++i) vr[i] = fetch(a.v, a.v_off, kt * BN + kg * C::KPT + i, dg, a);
+      for (int i = 0; i < C::PASS; ++i) {
+        const uint2 x = *reinterpret_cast<const uint2 *>(kb + cache_off[i]);
+        const uint2 y = *reinterpret_cast<const uint2 *>(vb + cache_off[i]);
+        kr[i] = make_uint4(x.x, x.y, 0, 0);
+        vr[i] = make_uint4(y.x, y.y, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::PASS; ++i) {
+        const int key = k0 + row0 + i * C::ROWS;
+        kr[i] = fetch_row(a.k, a.k_off, key, a);
+        vr[i] = fetch_row(a.v, a.v_off, key, a);
+      }
+    }
   }
 
-  __device__ __forceinline__ void store(int kt, const TileArgs &a, __bf16 *Ks, __bf16 *Vt) {
-    using C = Cfg<D>;
-    const int t = threadIdx.x;
-    const int kc = t % C::CH, kr0 = t / C::CH;
+  __device__ __forceinline__ void store(int kt, const TileArgs &a, __bf16 *Ks, __bf16 *Vs) {
+    const int kd = tile_kind<SRC>(kt, a);
 #pragma unroll
-    for (int i = 0; i < C::KPASS; ++i) {
-      const int row = kr0 + i * C::KROWS;
-      uint4 val = kr[i];
-      if (SRC == SRC_CACHE_FP8 && kt * BN + row < a.lp) val = dequant8(val.x, val.y, a.k_scale);
-      *reinterpret_cast<uint4 *>(Ks + row * D + ((kc ^ (row & (C::CH - 1))) << 3)) = val;
-    }
-    const int dg = t % C::CH, kg = t / C::CH;
-    uint4 vals[C::KPT];
-#pragma unroll
-    for (int i = 0; i < C::KPT; ++i) {
-      vals[i] = vr[i];
-      if (SRC == SRC_CACHE_FP8 && kt * BN + kg * C::KPT + i < a.lp)
-        vals[i] = dequant8(vals[i].x, vals[i].y, a.v_scale);
-    }
-    const int pos = vpos(kg * C::KPT);
-#pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      const int j = d >> 1;
-      uint32_t w[C::KPT / 2];
-#pragma unroll
-      for (int q = 0; q < C::KPT / 2; ++q) {
-        const uint32_t A = word(vals[2 * q], j), B = word(vals[2 * q + 1], j);
-        w[q] = (d & 1) ? ((A >> 16) | (B & 0xffff0000u)) : ((A & 0xffffu) | (B << 16));
+    for (int i = 0; i < C::PASS; ++i) {
+      const int r = row0 + i * C::ROWS;
+      uint4 kv = kr[i], vv = vr[i];
+      if (kd == CACHED || (kd == MIXED && kt * BN + r < a.lp && kt * BN + r < a.kend)) {
+        kv = dequant8(kv.x, kv.y, a.k_scale);
+        vv = dequant8(vv.x, vv.y, a.v_scale);
       }
-      const int dim = dg * 8 + d;
-      __bf16 *dst = Vt + dim * BN + (((pos >> 3) ^ (dim & 7)) << 3) + (pos & 7);
-      if (C::KPT == 4)
-        *reinterpret_cast<uint2 *>(dst) = make_uint2(w[0], w[1 % (C::KPT / 2)]);
-      else
-        *reinterpret_cast<uint32_t *>(dst) = w[0];
+      *reinterpret_cast<uint4 *>(Ks + r * D + ((chunk ^ C::swz(r)) << 3)) = kv;
+      *reinterpret_cast<uint4 *>(Vs + r * D + ((chunk ^ C::swz(r)) << 3)) = vv;
     }
   }
 };
 
-// One key tile for one wavefront: scores, online softmax, PV.
+// Workgroup barrier without the implicit wait for outstanding memory operations that
+// __syncthreads() adds: the ping-pong loop waits for its own direct loads explicitly,
+// two periods after issuing them.  The memory clobber keeps the compiler from moving
+// LDS accesses across it; every LDS read before it has been consumed by an MFMA.
+__device__ __forceinline__ void bar() { asm volatile("s_barrier" ::: "memory"); }
+
+// ---------------------------------------------------------------------------------------
+// Per-wavefront pieces of one key tile.
+
 template <int D>
-__device__ __forceinline__ void compute_tile(const __bf16 *Ks, const __bf16 *Vt,
-                                             const bf16x8_t (&qf)[Cfg<D>::QS],
-                                             f32x16_t (&o)[Cfg<D>::DB], float &m_run,
-                                             float &l_run, int kt, int kend, float c) {
+__device__ __forceinline__ void qk_tile(const __bf16 *Ks, const bf16x8_t (&qf)[Cfg<D>::QS],
+                                        f32x16_t (&s)[2]) {
   using C = Cfg<D>;
   const int lane = threadIdx.x & 63;
   const int j = lane & 31, g = lane >> 5;
-
-  f32x16_t s[2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -191,13 +300,22 @@ __device__ __forceinline__ void compute_tile(const __bf16 *Ks, const __bf16 *Vt,
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int row = kb * 32 + j;
-      const int chunk = 2 * st + g;
+      const int ch = 2 * st + g;
       const bf16x8_t a =
-          *reinterpret_cast<const bf16x8_t *>(Ks + row * D + ((chunk ^ (row & (C::CH - 1))) << 3));
+          *reinterpret_cast<const bf16x8_t *>(Ks + row * D + ((ch ^ C::swz(row)) << 3));
       s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s[kb], 0, 0, 0);
     }
   }
+}
 
+// Mask the tail tile, take the row max, raise the running max when it is exceeded by
+// more than TAU (rescaling O and l exactly).
+template <int D>
+__device__ __forceinline__ void softmax_max(f32x16_t (&s)[2], f32x16_t (&o)[Cfg<D>::DB],
+                                            float &m_run, float &l_run, int kt, int kend,
+                                            float c) {
+  using C = Cfg<D>;
+  const int g = (threadIdx.x & 63) >> 5;
   if ((kt + 1) * BN > kend) {   // the PARTIAL tile: keys at or past kend do not exist
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -207,14 +325,12 @@ __device__ __forceinline__ void compute_tile(const __bf16 *Ks, const __bf16 *Vt,
         if (key >= kend) s[kb][r] = -INFINITY;
       }
   }
-
   float mx = s[0][0];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float mc = mx * c;
+  const float mc = pair_max(mx) * c;
   if (__any(mc > m_run + TAU)) {
     const float mn = fmaxf(m_run, mc);
     const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
@@ -225,8 +341,13 @@ __device__ __forceinline__ void compute_tile(const __bf16 *Ks, const __bf16 *Vt,
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
   }
+}
 
-  bf16x8_t p[2][2];
+// P = 2^(s c - m) in bf16, in the MFMA B-operand order: step (kb, cc) holds keys
+// 32kb + 16cc + {4g..4g+3, 8+4g..8+4g+3}, i.e. this lane's score registers 8cc..8cc+7.
+// The row sum accumulates the same bf16 values the PV product uses.
+__device__ __forceinline__ void softmax_exp(const f32x16_t (&s)[2], float m_run, float c,
+                                            float &l_run, bf16x8_t (&p)[2][2]) {
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
@@ -244,35 +365,87 @@ __device__ __forceinline__ void compute_tile(const __bf16 *Ks, const __bf16 *Vt,
       uint4 u = make_uint4(w[0], w[1], w[2], w[3]);
       p[kb][cc] = __builtin_bit_cast(bf16x8_t, u);
     }
+}
 
+// O^T += V^T P^T.  V^T fragments by transpose reads: in each 16-lane group (i = lane %
+// 16), lane i addresses 4 dims (4 (i % 4) + 16 ((lane / 16) & 1) + 32 db) of key row
+// (step base + 4 g + i / 4); the read hands lane i those 4 keys at dim (lane % 32) + 32 db.
+// Two reads (rows +0 and +8) give the 8 keys of one 16-key step.
+template <int D>
+__device__ __forceinline__ void pv_tile(const __bf16 *Vs, const bf16x8_t (&p)[2][2],
+                                        f32x16_t (&o)[Cfg<D>::DB]) {
+  using C = Cfg<D>;
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 5;
+  const int i16 = lane & 15;
+  const int rsub = i16 >> 2;
+  const int dsub = 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) {
-    const int dim = db * 32 + j;
+    const int dim = db * 32 + dsub;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
-        const int chunk = 4 * kb + 2 * cc + g;
-        const bf16x8_t a =
-            *reinterpret_cast<const bf16x8_t *>(Vt + dim * BN + ((chunk ^ (dim & 7)) << 3));
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p[kb][cc], o[db], 0, 0, 0);
+        i16x4_t h[2];
+#pragma unroll
+        for (int r8 = 0; r8 < 2; ++r8) {
+          const int row = 32 * kb + 16 * cc + 8 * r8 + 4 * g + rsub;
+          const __bf16 *src = Vs + row * D + (((dim >> 3) ^ C::swz(row)) << 3) + (dim & 7);
+          h[r8] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(src));
+        }
+        const i16x8_t both = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, both),
+                                                         p[kb][cc], o[db], 0, 0, 0);
       }
   }
 }
 
-template <int D, int SRC>
-__global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(
-    const int32_t *__restrict__ sched, const qi_tile *__restrict__ tiles, int H,
-    const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
-    __bf16 *__restrict__ o, const uint8_t *__restrict__ cache, float c) {
-  using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 lds[2][2 * C::TILE];
+// ---------------------------------------------------------------------------------------
+// Common prologue / epilogue.
 
-  const int item = sched[blockIdx.x];
-  if (item < 0) return;   // schedule padding
-  const qi_tile tl = tiles[item / H];
-  const int h = item % H;
+struct Work {
+  qi_tile tl;
+  int h;
+};
 
+template <int D>
+__device__ __forceinline__ void load_q(const __bf16 *q, const qi_tile &tl, int H, int h,
+                                       bf16x8_t (&qf)[Cfg<D>::QS]) {
+  const int lane = threadIdx.x & 63;
+  const int row = (threadIdx.x >> 6) * 32 + (lane & 31);
+  const bool valid = row < tl.nrows;
+  const __bf16 *qp = q + ((int64_t)(tl.q_tok + row) * H + h) * D + 8 * (lane >> 5);
+#pragma unroll
+  for (int st = 0; st < Cfg<D>::QS; ++st) {
+    uint4 u = valid ? *reinterpret_cast<const uint4 *>(qp + 16 * st) : make_uint4(0, 0, 0, 0);
+    qf[st] = __builtin_bit_cast(bf16x8_t, u);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_o(__bf16 *o, const qi_tile &tl, int H, int h,
+                                        const f32x16_t (&acc)[Cfg<D>::DB], float l_run) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 5;
+  const int row = (threadIdx.x >> 6) * 32 + (lane & 31);
+  const float inv = 1.0f / pair_sum(l_run);
+  if (row >= tl.nrows) return;
+  __bf16 *op = o + ((int64_t)(tl.q_tok + row) * H + h) * D;
+#pragma unroll
+  for (int db = 0; db < Cfg<D>::DB; ++db)
+#pragma unroll
+    for (int aa = 0; aa < 4; ++aa) {
+      const int dim = db * 32 + 8 * aa + 4 * g;
+      uint2 u;
+      u.x = pack_bf16(acc[db][4 * aa] * inv, acc[db][4 * aa + 1] * inv);
+      u.y = pack_bf16(acc[db][4 * aa + 2] * inv, acc[db][4 * aa + 3] * inv);
+      *reinterpret_cast<uint2 *>(op + dim) = u;
+    }
+}
+
+__device__ __forceinline__ TileArgs make_args(const qi_tile &tl, int H, int h, const __bf16 *k,
+                                              const __bf16 *v, const uint8_t *cache, bool fp8) {
   TileArgs a;
   a.k = k;
   a.v = v;
@@ -286,27 +459,55 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(
   a.v_off = tl.v_off;
   a.k_scale = 1.0f;
   a.v_scale = 1.0f;
-  if (SRC == SRC_CACHE_FP8) {
+  if (fp8) {
     const float *sc = reinterpret_cast<const float *>(cache + tl.s_off);
     a.k_scale = sc[h];
     a.v_scale = sc[H + h];
   }
+  return a;
+}
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int j = lane & 31, g = lane >> 5;
-  const int row = wave * 32 + j;               // row inside the tile
-  const bool active = wave * 32 < tl.nrows;    // wavefront has at least one real row
+// ---------------------------------------------------------------------------------------
+// Ping-pong kernel (bf16 sources).
+//
+// Every wavefront runs, for tile j = 0 .. n:
+//   MFMA phase j: S = QK^T(K_j) (j < n);  O += PV(V_{j-1}, P) (j > 0)
+//   barrier
+//   VALU phase j: P = softmax(S) (j < n), rescaling O when the running max rises
+//   barrier
+// Group 1 (wavefronts 4..7) starts one barrier late and group 0 ends one barrier late,
+// so between consecutive barriers ("periods") one group is in an MFMA phase and the
+// other in a VALU phase: group 0 runs MFMA phase t in period 2t, group 1 in period 2t+1.
+// K_t and V_{t-1} are read in periods 2t and 2t+1.
+// Direct loads of a half tile are issued only after a barrier that follows the last
+// read of the buffer they overwrite by every wavefront of both groups:
+//   group 0, end of period 2t:   its half of K_{t+1} and V_t (buffers last read in
+//                                period 2t-1; group 0 reads other buffers in 2t)
+//   group 1, start of 2t+2:      its half of K_{t+2} and V_{t+1} (buffers last read in
+//                                period 2t+1)
+// and each wavefront waits for its own loads (s_waitcnt) before a barrier that precedes
+// their first reader: group 0 at the end of period 2t+1, group 1 at the end of period
+// 2t+3; group 0 first reads them in period 2t+2 resp. 2t+4.
+template <int D, int SRC>
+__global__ __launch_bounds__(NT, 1) void attn_pp_kernel(
+    const int32_t *__restrict__ sched, const qi_tile *__restrict__ tiles, int H,
+    const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
+    __bf16 *__restrict__ o, const uint8_t *__restrict__ cache, float c) {
+  using C = Cfg<D>;
+  __shared__ __attribute__((aligned(1024))) __bf16 Kb[2][C::TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 Vb[2][C::TILE];
+
+  const int item = sched[blockIdx.x];
+  if (item < 0) return;   // schedule padding
+  const qi_tile tl = tiles[item / H];
+  const int h = item % H;
+  const TileArgs a = make_args(tl, H, h, k, v, cache, false);
+  const int wave = threadIdx.x >> 6;
+  const int group = wave >> 2;
+  const bool active = wave * 32 < tl.nrows;   // wavefront has a real row
 
   bf16x8_t qf[C::QS];
-  {
-    const bool valid = row < tl.nrows;
-    const __bf16 *qp = q + ((int64_t)(tl.q_tok + row) * H + h) * D + 8 * g;
-#pragma unroll
-    for (int st = 0; st < C::QS; ++st) {
-      uint4 u = valid ? *reinterpret_cast<const uint4 *>(qp + 16 * st) : make_uint4(0, 0, 0, 0);
-      qf[st] = __builtin_bit_cast(bf16x8_t, u);
-    }
-  }
+  load_q<D>(q, tl, H, h, qf);
   f32x16_t acc[C::DB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
@@ -314,37 +515,102 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
 
-  const int ntiles = (tl.kend + BN - 1) / BN;
+  const int n = (tl.kend + BN - 1) / BN;
+  Direct<D, SRC> dm;
+  dm.init(a);
+  // prologue: K_0 complete for everyone; K_1 and V_0 issued by both groups
+  dm.issue(0, a, a.k, a.k_off, Kb[0]);
+  if (n > 1) dm.issue(1, a, a.k, a.k_off, Kb[1]);
+  dm.issue(0, a, a.v, a.v_off, Vb[0]);
+  __builtin_amdgcn_s_waitcnt(0);
+  bar();
+  if (group == 1) bar();                   // group 1 idles through period 0
+
+  f32x16_t s[2];
+  bf16x8_t p[2][2];
+  for (int t = 0; t <= n; ++t) {
+    // ---- MFMA phase t
+    __builtin_amdgcn_s_setprio(1);
+    if (active) {
+      if (t < n) qk_tile<D>(Kb[t & 1], qf, s);
+      if (t > 0) pv_tile<D>(Vb[(t - 1) & 1], p, acc);
+    }
+    __builtin_amdgcn_s_setprio(0);
+    if (group == 0) {
+      if (t + 1 < n && t >= 1) {           // t = 0: issued in the prologue
+        dm.issue(t + 1, a, a.k, a.k_off, Kb[(t + 1) & 1]);
+        dm.issue(t, a, a.v, a.v_off, Vb[t & 1]);
+      } else if (t + 1 == n && t >= 1) {
+        dm.issue(t, a, a.v, a.v_off, Vb[t & 1]);
+      }
+    } else {
+      __builtin_amdgcn_s_waitcnt(0);       // group 1: loads issued two periods ago
+    }
+    bar();
+    // ---- VALU phase t
+    if (group == 1) {                      // all of group 1 has finished MFMA phase t
+      if (t + 2 < n) dm.issue(t + 2, a, a.k, a.k_off, Kb[t & 1]);
+      if (t + 1 < n) dm.issue(t + 1, a, a.v, a.v_off, Vb[(t + 1) & 1]);
+    }
+    if (active && t < n) {
+      softmax_max<D>(s, acc, m_run, l_run, t, tl.kend, c);
+      softmax_exp(s, m_run, c, l_run, p);
+    }
+    if (group == 0) __builtin_amdgcn_s_waitcnt(0);   // loads issued one period ago
+    bar();
+  }
+  if (group == 0) bar();
+  if (active) store_o<D>(o, tl, H, h, acc, l_run);
+}
+
+// ---------------------------------------------------------------------------------------
+// Register-staged kernel (fp8 cache): plain double-buffered loop.
+template <int D, int SRC>
+__global__ __launch_bounds__(NT, 1) void attn_staged_kernel(
+    const int32_t *__restrict__ sched, const qi_tile *__restrict__ tiles, int H,
+    const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
+    __bf16 *__restrict__ o, const uint8_t *__restrict__ cache, float c) {
+  using C = Cfg<D>;
+  __shared__ __attribute__((aligned(1024))) __bf16 lds[2][2 * C::TILE];
+
+  const int item = sched[blockIdx.x];
+  if (item < 0) return;
+  const qi_tile tl = tiles[item / H];
+  const int h = item % H;
+  const TileArgs a = make_args(tl, H, h, k, v, cache, SRC == SRC_CACHE_FP8);
+  const bool active = (threadIdx.x >> 6) * 32 < tl.nrows;
+
+  bf16x8_t qf[C::QS];
+  load_q<D>(q, tl, H, h, qf);
+  f32x16_t acc[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  const int n = (tl.kend + BN - 1) / BN;
   Stage<D, SRC> st;
+  st.init(a);
   st.load(0, a);
   st.store(0, a, lds[0], lds[0] + C::TILE);
-  if (ntiles > 1) st.load(1, a);
+  if (n > 1) st.load(1, a);
   __syncthreads();
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int cur = kt & 1;
-    if (active)
-      compute_tile<D>(lds[cur], lds[cur] + C::TILE, qf, acc, m_run, l_run, kt, tl.kend, c);
-    if (kt + 1 < ntiles) st.store(kt + 1, a, lds[cur ^ 1], lds[cur ^ 1] + C::TILE);
-    if (kt + 2 < ntiles) st.load(kt + 2, a);
+  for (int j = 0; j < n; ++j) {
+    const int cur = j & 1;
+    if (active) {
+      f32x16_t s[2];
+      bf16x8_t p[2][2];
+      qk_tile<D>(lds[cur], qf, s);
+      softmax_max<D>(s, acc, m_run, l_run, j, tl.kend, c);
+      softmax_exp(s, m_run, c, l_run, p);
+      pv_tile<D>(lds[cur] + C::TILE, p, acc);
+    }
+    if (j + 1 < n) st.store(j + 1, a, lds[cur ^ 1], lds[cur ^ 1] + C::TILE);
+    if (j + 2 < n) st.load(j + 2, a);
     __syncthreads();
   }
-
-  if (!active) return;
-  const float lt = l_run + __shfl_xor(l_run, 32);
-  const float inv = 1.0f / lt;
-  if (row < tl.nrows) {
-    __bf16 *op = o + ((int64_t)(tl.q_tok + row) * H + h) * D;
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-      for (int aa = 0; aa < 4; ++aa) {
-        const int dim = db * 32 + 8 * aa + 4 * g;
-        uint2 u;
-        u.x = pack_bf16(acc[db][4 * aa] * inv, acc[db][4 * aa + 1] * inv);
-        u.y = pack_bf16(acc[db][4 * aa + 2] * inv, acc[db][4 * aa + 3] * inv);
-        *reinterpret_cast<uint2 *>(op + dim) = u;
-      }
-  }
+  if (active) store_o<D>(o, tl, H, h, acc, l_run);
 }
 
 template <int D, int SRC>
@@ -352,7 +618,8 @@ qi_status launch(const qi_plan *p, int call, const void *q, const void *k, const
                  void *o, const void *cache, hipStream_t s) {
   const uint8_t *ws = static_cast<const uint8_t *>(p->d_ws);
   const float c = (float)(1.4426950408889634 / std::sqrt((double)D));   // log2(e)/sqrt(D)
-  hipLaunchKernelGGL((attn_fwd_kernel<D, SRC>), dim3(p->sched_len[call]), dim3(NT), 0, s,
+  auto kern = SRC == SRC_CACHE_FP8 ? attn_staged_kernel<D, SRC> : attn_pp_kernel<D, SRC>;
+  hipLaunchKernelGGL(kern, dim3(p->sched_len[call]), dim3(NT), 0, s,
                      reinterpret_cast<const int32_t *>(ws + p->sched_off[call]),
                      reinterpret_cast<const qi_tile *>(ws + p->tiles_off[call]), p->H,
                      static_cast<const __bf16 *>(q), static_cast<const __bf16 *>(k),
