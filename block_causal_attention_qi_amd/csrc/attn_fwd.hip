@@ -1,8 +1,8 @@
 // Block-causal attention forward for gfx950 (CDNA4), bf16 MFMA, fp32 online softmax.
 //
-// One workgroup (8 wavefronts, 512 lanes) owns one (request, head, row tile of <= 256
-// rows); each wavefront owns 32 query rows and keeps its Q fragments and its O
-// accumulator in registers for the whole key loop.  Row tiles never cross a block, so
+// One workgroup owns one (request, head, row tile of <= 128 rows); each wavefront owns
+// 32 query rows and keeps its Q fragments and its O accumulator in registers for the
+// whole key loop.  Row tiles never cross a block, so
 // every row of a tile sees the same key prefix [0, kend) (block-causal rule: a row of
 // block b sees keys of blocks 0..b; ThakiCloud blog "Qwen-Image-2.1 vLLM-Omni day 0",
 // section "Serving architecture: the cross-step prefix KV cache").  Key tiles past kend
@@ -33,14 +33,17 @@
 // access of the kernel is free of bank conflicts on the 64-bank gfx950 LDS (16 lanes per
 // cycle for 16-byte reads, 32 lanes per cycle for 8-byte reads).
 //
-// Workgroup: 8 wavefronts (two per SIMD) own 256 query rows; they form two groups of four
-// that alternate phases ("ping-pong"): while one group runs its MFMA phase (QK^T of key
-// tile j and PV of tile j-1) the other runs its VALU phase (softmax of its tile), and the
-// two swap at every workgroup barrier, so each SIMD always has one wavefront feeding the
-// matrix core and one feeding the vector ALU.  The MFMA-phase wavefront raises its issue
-// priority.  bf16 tiles go straight from global memory into LDS (global_load_lds_dwordx4,
-// no staging registers), double-buffered, one tile ahead.  The fp8 cache is staged
-// through registers, where its codes are dequantised, with a plain loop.
+// bf16 sources (full call, prefix call, denoising call on a bf16 cache): a workgroup of
+// 8 wavefronts (two per SIMD) owns 128 query rows; wavefronts w and w+4 hold the same 32
+// rows, and the two groups of four split the key tiles (group 0 the even ones, group 1
+// the odd ones).  The groups alternate phases ("ping-pong"): while one runs its MFMA
+// phase (QK^T of its tile j and PV of its tile j-2) the other runs its VALU phase
+// (softmax of its tile j-1) and loads its next tiles straight from global memory into
+// LDS (global_load_lds_dwordx4, no staging registers); the two swap at every workgroup
+// barrier, so each SIMD always has one wavefront feeding the matrix core and one feeding
+// the vector ALU.  At the end the two partial softmax states (m, l, O) of each row are
+// merged through LDS in a fixed order.  The fp8 cache is staged through registers,
+// where its codes are dequantised, by 4 wavefronts with a plain loop.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -59,8 +62,8 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int BM = QI_KERNEL_BM;
 constexpr int BN = QI_KERNEL_BN;
-constexpr int NT = 512;                 // 8 wavefronts
-constexpr int NWAVE = NT / 64;
+constexpr int NT = 512;                 // ping-pong kernel: 8 wavefronts
+constexpr int NT_STAGED = 256;          // register-staged kernel: 4 wavefronts
 constexpr float TAU = 8.0f;   // lazy-rescale threshold, log2 units
 
 enum { SRC_ONE = 0, SRC_CACHE_BF16 = 1, SRC_CACHE_FP8 = 2 };
@@ -68,14 +71,14 @@ enum { SRC_ONE = 0, SRC_CACHE_BF16 = 1, SRC_CACHE_FP8 = 2 };
 template <int D>
 struct Cfg {
   static constexpr int CH = D / 8;           // 16-byte chunks per K/V row
-  static constexpr int ROWS = NT / CH;       // rows staged per pass (all 256 lanes)
-  static constexpr int PASS = BN / ROWS;     // passes per tile
+  static constexpr int ROWS = NT_STAGED / CH;   // rows staged per pass (register staging)
+  static constexpr int PASS = BN / ROWS;        // passes per tile
   static constexpr int QS = D / 16;          // MFMA k-steps over the head dim
   static constexpr int DB = D / 32;          // 32-wide blocks of the output
   static constexpr int TILE = BN * D;        // bf16 elements per staged K (or V) tile
-  static constexpr int IPW = D / 64;         // 1 KiB direct loads per wavefront per tile
+  static constexpr int IPW = D / 32;         // 1 KiB direct loads per wavefront per tile
   static constexpr int RPK = 512 / D;        // rows per 1 KiB
-  static_assert(PASS * ROWS == BN && IPW * RPK * NWAVE == BN, "tile shape");
+  static_assert(PASS * ROWS == BN && IPW * RPK * 4 == BN, "tile shape");
   // Physical 16-byte chunk = logical chunk ^ swz(row).  One swizzle serves both tiles:
   //  K reads: 16 lanes read one chunk of 16 consecutive rows -> 16 distinct bank groups;
   //  V transpose reads: 32 lanes read 64 bytes of 4 consecutive rows -> 64 distinct banks.
@@ -134,10 +137,10 @@ __device__ __forceinline__ int tile_kind(int kt, const TileArgs &a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Direct global -> LDS tile loads (bf16 sources).  Instruction i of wavefront w fills the
-// i-th KiB of the wavefront's share of a tile: lane l writes the 16 bytes at KiB offset
-// 16 l, i.e. row (w * IPW + i) * RPK + l / CH, physical chunk l % CH, so it loads logical
-// chunk (l % CH) ^ swz(row) of that key row.
+// Direct global -> LDS tile loads (bf16 sources).  The four wavefronts of one group load
+// a tile; instruction i of wavefront w (w = wave % 4) fills the i-th KiB of its share:
+// lane l writes the 16 bytes at KiB offset 16 l, i.e. row (w * IPW + i) * RPK + l / CH,
+// physical chunk l % CH, so it loads logical chunk (l % CH) ^ swz(row) of that key row.
 template <int D, int SRC>
 struct Direct {
   using C = Cfg<D>;
@@ -145,7 +148,7 @@ struct Direct {
   int cache_off[C::IPW];   // element offsets inside one cached head, from the tile's key 0
 
   __device__ __forceinline__ static int row_of(int i) {
-    return ((threadIdx.x >> 6) * C::IPW + i) * C::RPK + (threadIdx.x & 63) / C::CH;
+    return (((threadIdx.x >> 6) & 3) * C::IPW + i) * C::RPK + (threadIdx.x & 63) / C::CH;
   }
   __device__ __forceinline__ static int chunk_of(int i) {
     return ((threadIdx.x & 63) % C::CH) ^ C::swz(row_of(i));
@@ -160,7 +163,7 @@ struct Direct {
   }
 
   __device__ __forceinline__ static void dma(const __bf16 *src, __bf16 *tile, int i) {
-    __bf16 *dst = tile + ((threadIdx.x >> 6) * C::IPW + i) * 512;   // wavefront-uniform
+    __bf16 *dst = tile + (((threadIdx.x >> 6) & 3) * C::IPW + i) * 512;   // wavefront-uniform
     __builtin_amdgcn_global_load_lds(src, (lds_void_t *)dst, 16, 0, 0);
   }
 
@@ -207,7 +210,7 @@ struct Stage {
   int cache_off[C::PASS];
 
   __device__ __forceinline__ void init(const TileArgs &a) {
-    row0 = threadIdx.x / C::CH;
+    row0 = threadIdx.x / C::CH;      // NT_STAGED lanes
     chunk = threadIdx.x % C::CH;
 #pragma unroll
     for (int i = 0; i < C::PASS; ++i) {
@@ -413,7 +416,7 @@ template <int D>
 __device__ __forceinline__ void load_q(const __bf16 *q, const qi_tile &tl, int H, int h,
                                        bf16x8_t (&qf)[Cfg<D>::QS]) {
   const int lane = threadIdx.x & 63;
-  const int row = (threadIdx.x >> 6) * 32 + (lane & 31);
+  const int row = ((threadIdx.x >> 6) & 3) * 32 + (lane & 31);
   const bool valid = row < tl.nrows;
   const __bf16 *qp = q + ((int64_t)(tl.q_tok + row) * H + h) * D + 8 * (lane >> 5);
 #pragma unroll
@@ -428,7 +431,7 @@ __device__ __forceinline__ void store_o(__bf16 *o, const qi_tile &tl, int H, int
                                         const f32x16_t (&acc)[Cfg<D>::DB], float l_run) {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 5;
-  const int row = (threadIdx.x >> 6) * 32 + (lane & 31);
+  const int row = ((threadIdx.x >> 6) & 3) * 32 + (lane & 31);
   const float inv = 1.0f / pair_sum(l_run);
   if (row >= tl.nrows) return;
   __bf16 *op = o + ((int64_t)(tl.q_tok + row) * H + h) * D;
@@ -470,32 +473,30 @@ __device__ __forceinline__ TileArgs make_args(const qi_tile &tl, int H, int h, c
 // ---------------------------------------------------------------------------------------
 // Ping-pong kernel (bf16 sources).
 //
-// Every wavefront runs, for tile j = 0 .. n:
-//   MFMA phase j: S = QK^T(K_j) (j < n);  O += PV(V_{j-1}, P) (j > 0)
-//   barrier
-//   VALU phase j: P = softmax(S) (j < n), rescaling O when the running max rises
-//   barrier
-// Group 1 (wavefronts 4..7) starts one barrier late and group 0 ends one barrier late,
-// so between consecutive barriers ("periods") one group is in an MFMA phase and the
-// other in a VALU phase: group 0 runs MFMA phase t in period 2t, group 1 in period 2t+1.
-// K_t and V_{t-1} are read in periods 2t and 2t+1.
-// Direct loads of a half tile are issued only after a barrier that follows the last
-// read of the buffer they overwrite by every wavefront of both groups:
-//   group 0, end of period 2t:   its half of K_{t+1} and V_t (buffers last read in
-//                                period 2t-1; group 0 reads other buffers in 2t)
-//   group 1, start of 2t+2:      its half of K_{t+2} and V_{t+1} (buffers last read in
-//                                period 2t+1)
-// and each wavefront waits for its own loads (s_waitcnt) before a barrier that precedes
-// their first reader: group 0 at the end of period 2t+1, group 1 at the end of period
-// 2t+3; group 0 first reads them in period 2t+2 resp. 2t+4.
+// Key tile t belongs to group t & 1.  Period p (p = 0 .. n+1, one barrier each):
+//   MFMA group (p & 1):       S = QK^T(K_p) if p < n;  O += PV(V_{p-2}, P) if p >= 2
+//   VALU group ((p + 1) & 1): P = softmax(S of tile p-1) if 1 <= p <= n; then it waits
+//                             for the loads it issued two periods ago and issues those
+//                             its own MFMA phase reads in period p+3: K_{p+3} and V_{p+1}.
+// Tile t of K lives in ring slot t & 3 and tile t of V in slot t & 3 (four separate LDS
+// arrays each, so the compiler can tell every load target from every buffer being read
+// and never stalls a read on an unrelated load).  The loads issued at the end of period
+// p overwrite K_{p-1} and V_{p-3}, both last read in period p-1, and are complete and
+// published by the barrier that ends period p+2.  K_0, K_1, K_2 and V_0 are loaded before
+// period 0.  The period loop is unrolled by four so that every slot index is a constant.
+// Afterwards group 1 stores its (m, l, O) in LDS and group 0 merges them into its own
+// (fixed order) and writes the rows.
+template <int P> struct Slot { static constexpr int value = P; };
+
 template <int D, int SRC>
 __global__ __launch_bounds__(NT, 1) void attn_pp_kernel(
     const int32_t *__restrict__ sched, const qi_tile *__restrict__ tiles, int H,
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     __bf16 *__restrict__ o, const uint8_t *__restrict__ cache, float c) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(1024))) __bf16 Kb[2][C::TILE];
-  __shared__ __attribute__((aligned(1024))) __bf16 Vb[2][C::TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 K0[C::TILE], K1[C::TILE], K2[C::TILE], K3[C::TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 V0[C::TILE], V1[C::TILE], V2[C::TILE], V3[C::TILE];
+#define QI_RING(arr, i) ((i) == 0 ? arr##0 : (i) == 1 ? arr##1 : (i) == 2 ? arr##2 : arr##3)
 
   const int item = sched[blockIdx.x];
   if (item < 0) return;   // schedule padding
@@ -504,7 +505,7 @@ __global__ __launch_bounds__(NT, 1) void attn_pp_kernel(
   const TileArgs a = make_args(tl, H, h, k, v, cache, false);
   const int wave = threadIdx.x >> 6;
   const int group = wave >> 2;
-  const bool active = wave * 32 < tl.nrows;   // wavefront has a real row
+  const bool active = (wave & 3) * 32 < tl.nrows;   // the wavefront's rows exist
 
   bf16x8_t qf[C::QS];
   load_q<D>(q, tl, H, h, qf);
@@ -518,55 +519,78 @@ __global__ __launch_bounds__(NT, 1) void attn_pp_kernel(
   const int n = (tl.kend + BN - 1) / BN;
   Direct<D, SRC> dm;
   dm.init(a);
-  // prologue: K_0 complete for everyone; K_1 and V_0 issued by both groups
-  dm.issue(0, a, a.k, a.k_off, Kb[0]);
-  if (n > 1) dm.issue(1, a, a.k, a.k_off, Kb[1]);
-  dm.issue(0, a, a.v, a.v_off, Vb[0]);
+  // prologue: K_0, K_1, K_2 and V_0, each half loaded by one group
+  {
+    __bf16 *dst = group == 0 ? K0 : K1;
+    if (group == 0 || n > 1) dm.issue(group, a, a.k, a.k_off, dst);
+    if (group == 0 && n > 2) dm.issue(2, a, a.k, a.k_off, K2);
+    if (group == 1) dm.issue(0, a, a.v, a.v_off, V0);
+  }
   __builtin_amdgcn_s_waitcnt(0);
   bar();
-  if (group == 1) bar();                   // group 1 idles through period 0
 
   f32x16_t s[2];
   bf16x8_t p[2][2];
-  for (int t = 0; t <= n; ++t) {
-    // ---- MFMA phase t
-    __builtin_amdgcn_s_setprio(1);
-    if (active) {
-      if (t < n) qk_tile<D>(Kb[t & 1], qf, s);
-      if (t > 0) pv_tile<D>(Vb[(t - 1) & 1], p, acc);
-    }
-    __builtin_amdgcn_s_setprio(0);
-    if (group == 0) {
-      if (t + 1 < n && t >= 1) {           // t = 0: issued in the prologue
-        dm.issue(t + 1, a, a.k, a.k_off, Kb[(t + 1) & 1]);
-        dm.issue(t, a, a.v, a.v_off, Vb[t & 1]);
-      } else if (t + 1 == n && t >= 1) {
-        dm.issue(t, a, a.v, a.v_off, Vb[t & 1]);
+  auto period = [&](auto slot, int per) {
+    constexpr int P = decltype(slot)::value;   // per & 3
+    if ((P & 1) == group) {
+      __builtin_amdgcn_s_setprio(1);
+      if (active) {
+        if (per < n) qk_tile<D>(QI_RING(K, P), qf, s);
+        if (per >= 2) pv_tile<D>(QI_RING(V, (P + 2) & 3), p, acc);
       }
+      __builtin_amdgcn_s_setprio(0);
     } else {
-      __builtin_amdgcn_s_waitcnt(0);       // group 1: loads issued two periods ago
+      if (active && per >= 1 && per <= n) {
+        softmax_max<D>(s, acc, m_run, l_run, per - 1, tl.kend, c);
+        softmax_exp(s, m_run, c, l_run, p);
+      }
+      __builtin_amdgcn_s_waitcnt(0);   // this group's loads of two periods ago
+      if (per + 3 < n) dm.issue(per + 3, a, a.k, a.k_off, QI_RING(K, (P + 3) & 3));
+      if (per + 1 < n) dm.issue(per + 1, a, a.v, a.v_off, QI_RING(V, (P + 1) & 3));
     }
     bar();
-    // ---- VALU phase t
-    if (group == 1) {                      // all of group 1 has finished MFMA phase t
-      if (t + 2 < n) dm.issue(t + 2, a, a.k, a.k_off, Kb[t & 1]);
-      if (t + 1 < n) dm.issue(t + 1, a, a.v, a.v_off, Vb[(t + 1) & 1]);
-    }
-    if (active && t < n) {
-      softmax_max<D>(s, acc, m_run, l_run, t, tl.kend, c);
-      softmax_exp(s, m_run, c, l_run, p);
-    }
-    if (group == 0) __builtin_amdgcn_s_waitcnt(0);   // loads issued one period ago
-    bar();
+  };
+  for (int p0 = 0; p0 <= n + 1; p0 += 4) {
+    period(Slot<0>(), p0);
+    if (p0 + 1 <= n + 1) period(Slot<1>(), p0 + 1);
+    if (p0 + 2 <= n + 1) period(Slot<2>(), p0 + 2);
+    if (p0 + 3 <= n + 1) period(Slot<3>(), p0 + 3);
   }
-  if (group == 0) bar();
-  if (active) store_o<D>(o, tl, H, h, acc, l_run);
+#undef QI_RING
+
+  // merge the two partial states of each row (group 1 -> LDS -> group 0); the tile
+  // buffers are free: every load was waited for and every read consumed
+  const int w4 = wave & 3, lane = threadIdx.x & 63;
+  float *ost = reinterpret_cast<float *>(w4 == 0 ? K0 : w4 == 1 ? K1 : w4 == 2 ? K2 : K3) + lane;
+  float *mst = reinterpret_cast<float *>(V0) + (w4 * 64 + lane) * 2;
+  if (group == 1 && active) {
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ost[(16 * db + r) * 64] = acc[db][r];
+    mst[0] = m_run;
+    mst[1] = l_run;
+  }
+  __syncthreads();
+  if (group == 0 && active) {
+    const float m1 = mst[0], l1 = mst[1];
+    const float mm = fmaxf(m_run, m1);
+    const float a0 = __builtin_amdgcn_exp2f(m_run - mm);
+    const float a1 = __builtin_amdgcn_exp2f(m1 - mm);   // 0 when group 1 saw no tile
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[db][r] = acc[db][r] * a0 + ost[(16 * db + r) * 64] * a1;
+    l_run = l_run * a0 + l1 * a1;
+    store_o<D>(o, tl, H, h, acc, l_run);
+  }
 }
 
 // ---------------------------------------------------------------------------------------
 // Register-staged kernel (fp8 cache): plain double-buffered loop.
 template <int D, int SRC>
-__global__ __launch_bounds__(NT, 1) void attn_staged_kernel(
+__global__ __launch_bounds__(NT_STAGED, 2) void attn_staged_kernel(
     const int32_t *__restrict__ sched, const qi_tile *__restrict__ tiles, int H,
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     __bf16 *__restrict__ o, const uint8_t *__restrict__ cache, float c) {
@@ -619,7 +643,8 @@ qi_status launch(const qi_plan *p, int call, const void *q, const void *k, const
   const uint8_t *ws = static_cast<const uint8_t *>(p->d_ws);
   const float c = (float)(1.4426950408889634 / std::sqrt((double)D));   // log2(e)/sqrt(D)
   auto kern = SRC == SRC_CACHE_FP8 ? attn_staged_kernel<D, SRC> : attn_pp_kernel<D, SRC>;
-  hipLaunchKernelGGL(kern, dim3(p->sched_len[call]), dim3(NT), 0, s,
+  const int nt = SRC == SRC_CACHE_FP8 ? NT_STAGED : NT;
+  hipLaunchKernelGGL(kern, dim3(p->sched_len[call]), dim3(nt), 0, s,
                      reinterpret_cast<const int32_t *>(ws + p->sched_off[call]),
                      reinterpret_cast<const qi_tile *>(ws + p->tiles_off[call]), p->H,
                      static_cast<const __bf16 *>(q), static_cast<const __bf16 *>(k),

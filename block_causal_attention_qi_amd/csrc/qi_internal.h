@@ -9,8 +9,8 @@
 
 #include "../../include/qi.h"
 
-// Attention tile: rows per workgroup (8 wavefronts x 32 query rows) x keys per step.
-#define QI_KERNEL_BM 256
+// Attention tile: rows per workgroup (4 x 32 query rows; the ping-pong kernel splits keys over two groups) x keys per step.
+#define QI_KERNEL_BM 128
 #define QI_KERNEL_BN 64
 // Number of XCDs of the MI355X; workgroups are dealt to them round-robin in launch order.
 #define QI_NUM_XCD 8
