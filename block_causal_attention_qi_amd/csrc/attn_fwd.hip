@@ -383,13 +383,15 @@ __device__ __forceinline__ void pv_tile(const __bf16 *Vs, const bf16x8_t (&p)[2]
   const int i16 = lane & 15;
   const int rsub = i16 >> 2;
   const int dsub = 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);
+  // the four output blocks are independent accumulation chains: interleave them so that
+  // consecutive MFMAs never wait on each other's results
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db) {
-    const int dim = db * 32 + dsub;
+  for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
+      for (int db = 0; db < C::DB; ++db) {
+        const int dim = db * 32 + dsub;
         i16x4_t h[2];
 #pragma unroll
         for (int r8 = 0; r8 < 2; ++r8) {
@@ -401,7 +403,6 @@ __device__ __forceinline__ void pv_tile(const __bf16 *Vs, const bf16x8_t (&p)[2]
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, both),
                                                          p[kb][cc], o[db], 0, 0, 0);
       }
-  }
 }
 
 // ---------------------------------------------------------------------------------------

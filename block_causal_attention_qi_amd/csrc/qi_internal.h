@@ -7,7 +7,7 @@
 
 #include <vector>
 
-#include "../../include/qi.h"
+#include "qi.h"   // include/ of the repository, on the include path
 
 // Attention tile: rows per workgroup (4 x 32 query rows; the ping-pong kernel splits keys over two groups) x keys per step.
 #define QI_KERNEL_BM 128
