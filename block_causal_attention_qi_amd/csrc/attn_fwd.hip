@@ -60,7 +60,6 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr int BM = QI_KERNEL_BM;
 constexpr int BN = QI_KERNEL_BN;
 constexpr int NT = 512;                 // ping-pong kernel: 8 wavefronts
 constexpr int NT_STAGED = 256;          // register-staged kernel: 4 wavefronts
@@ -137,63 +136,66 @@ __device__ __forceinline__ int tile_kind(int kt, const TileArgs &a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Direct global -> LDS tile loads (bf16 sources).  The four wavefronts of one group load
-// a tile; instruction i of wavefront w (w = wave % 4) fills the i-th KiB of its share:
-// lane l writes the 16 bytes at KiB offset 16 l, i.e. row (w * IPW + i) * RPK + l / CH,
-// physical chunk l % CH, so it loads logical chunk (l % CH) ^ swz(row) of that key row.
+// Direct global -> LDS tile loads (bf16 sources).  A tile is 64 x D bf16, i.e. 16 (D=128)
+// or 8 (D=64) KiB; the four wavefronts of one group each fill consecutive KiB of it (all
+// of it, or one half).  In KiB `kib` lane l writes the 16 bytes at offset 16 l: row
+// kib * RPK + l / CH, physical chunk l % CH, so it loads logical chunk (l % CH) ^ swz(row)
+// of that key row.
 template <int D, int SRC>
 struct Direct {
   using C = Cfg<D>;
-  int live_off[C::IPW];    // element offsets inside the live tensor, from the tile's key 0
-  int cache_off[C::IPW];   // element offsets inside one cached head, from the tile's key 0
+  __device__ __forceinline__ void init(const TileArgs &) {}
 
-  __device__ __forceinline__ static int row_of(int i) {
-    return (((threadIdx.x >> 6) & 3) * C::IPW + i) * C::RPK + (threadIdx.x & 63) / C::CH;
-  }
-  __device__ __forceinline__ static int chunk_of(int i) {
-    return ((threadIdx.x & 63) % C::CH) ^ C::swz(row_of(i));
+  // lane l of the wavefront writes the 16 bytes at offset 16 l of KiB `kib` of the tile
+  __device__ __forceinline__ static void dma(const __bf16 *src, __bf16 *tile, int kib) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void_t *)(tile + kib * 512), 16, 0, 0);
   }
 
-  __device__ __forceinline__ void init(const TileArgs &a) {
-#pragma unroll
-    for (int i = 0; i < C::IPW; ++i) {
-      live_off[i] = row_of(i) * a.H * D + chunk_of(i) * 8;
-      cache_off[i] = row_of(i) * D + chunk_of(i) * 8;
-    }
-  }
-
-  __device__ __forceinline__ static void dma(const __bf16 *src, __bf16 *tile, int i) {
-    __bf16 *dst = tile + (((threadIdx.x >> 6) & 3) * C::IPW + i) * 512;   // wavefront-uniform
-    __builtin_amdgcn_global_load_lds(src, (lds_void_t *)dst, 16, 0, 0);
-  }
-
-  // issue the loads of tile kt of one tensor (K: live = a.k, coff = a.k_off)
+  // issue the loads of tile kt of one tensor (K: live = a.k, coff = a.k_off).  HALF < 0:
+  // the four wavefronts of the calling group load the whole tile; HALF = 0 / 1: they load
+  // the first / second half of its rows (the other group loads the rest).
+  template <int HALF = -1>
   __device__ __forceinline__ void issue(int kt, const TileArgs &a, const __bf16 *live,
-                                        int64_t coff, __bf16 *tile) const {
+                                        int64_t coff, __bf16 *tile, int half = 0) const {
+    constexpr int N = HALF < 0 ? C::IPW : C::IPW / 2;
+    const int i0 = HALF < 0 ? 0 : half * (C::IPW / 2) * 4;   // first KiB index offset
     const int k0 = kt * BN;
     const int kd = tile_kind<SRC>(kt, a);
     if (kd == LIVE) {
       const __bf16 *base = live + ((int64_t)(a.kv_tok + k0 - a.lp) * a.H + a.h) * D;
 #pragma unroll
-      for (int i = 0; i < C::IPW; ++i) dma(base + live_off[i], tile, i);
+      for (int i = 0; i < N; ++i) dma_at(base, tile, i0, i, N, true, a);
     } else if (SRC != SRC_ONE && kd == CACHED) {
       const __bf16 *base =
           reinterpret_cast<const __bf16 *>(a.cache + coff) + (int64_t)(a.h * a.lp + k0) * D;
 #pragma unroll
-      for (int i = 0; i < C::IPW; ++i) dma(base + cache_off[i], tile, i);
+      for (int i = 0; i < N; ++i) dma_at(base, tile, i0, i, N, false, a);
     } else {
 #pragma unroll
-      for (int i = 0; i < C::IPW; ++i) {
+      for (int i = 0; i < N; ++i) {
+        const int kib = i0 + (threadIdx.x >> 6 & 3) * N + i;
+        const int row = kib * C::RPK + (threadIdx.x & 63) / C::CH;
+        const int chunk = ((threadIdx.x & 63) % C::CH) ^ C::swz(row);
         // keys past kend load key kend - 1: finite values of this request, masked later
-        const int key = min(k0 + row_of(i), a.kend - 1);
+        const int key = min(k0 + row, a.kend - 1);
         const __bf16 *src;
         if (SRC != SRC_ONE && key < a.lp)
           src = reinterpret_cast<const __bf16 *>(a.cache + coff) + (int64_t)(a.h * a.lp + key) * D;
         else
           src = live + ((int64_t)(a.kv_tok + key - a.lp) * a.H + a.h) * D;
-        dma(src + chunk_of(i) * 8, tile, i);
+        dma(src + chunk * 8, tile, kib);
       }
     }
+  }
+
+  // KiB kib = i0 + (wave % 4) * N + i of the tile, from a whole-tile base pointer
+  __device__ __forceinline__ static void dma_at(const __bf16 *base, __bf16 *tile, int i0, int i,
+                                                int N, bool live, const TileArgs &a) {
+    const int kib = i0 + (threadIdx.x >> 6 & 3) * N + i;
+    const int row = kib * C::RPK + (threadIdx.x & 63) / C::CH;
+    const int chunk = ((threadIdx.x & 63) % C::CH) ^ C::swz(row);
+    const int off = live ? row * a.H * D + chunk * 8 : row * D + chunk * 8;
+    dma(base + off, tile, kib);
   }
 };
 
@@ -413,11 +415,11 @@ struct Work {
   int h;
 };
 
+// row: this lane's query row inside the tile (lanes j and j + 32 share one row)
 template <int D>
-__device__ __forceinline__ void load_q(const __bf16 *q, const qi_tile &tl, int H, int h,
+__device__ __forceinline__ void load_q(const __bf16 *q, const qi_tile &tl, int H, int h, int row,
                                        bf16x8_t (&qf)[Cfg<D>::QS]) {
   const int lane = threadIdx.x & 63;
-  const int row = ((threadIdx.x >> 6) & 3) * 32 + (lane & 31);
   const bool valid = row < tl.nrows;
   const __bf16 *qp = q + ((int64_t)(tl.q_tok + row) * H + h) * D + 8 * (lane >> 5);
 #pragma unroll
@@ -428,11 +430,10 @@ __device__ __forceinline__ void load_q(const __bf16 *q, const qi_tile &tl, int H
 }
 
 template <int D>
-__device__ __forceinline__ void store_o(__bf16 *o, const qi_tile &tl, int H, int h,
+__device__ __forceinline__ void store_o(__bf16 *o, const qi_tile &tl, int H, int h, int row,
                                         const f32x16_t (&acc)[Cfg<D>::DB], float l_run) {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 5;
-  const int row = ((threadIdx.x >> 6) & 3) * 32 + (lane & 31);
   const float inv = 1.0f / pair_sum(l_run);
   if (row >= tl.nrows) return;
   __bf16 *op = o + ((int64_t)(tl.q_tok + row) * H + h) * D;
@@ -472,61 +473,143 @@ __device__ __forceinline__ TileArgs make_args(const qi_tile &tl, int H, int h, c
 }
 
 // ---------------------------------------------------------------------------------------
-// Ping-pong kernel (bf16 sources).
-//
-// Key tile t belongs to group t & 1.  Period p (p = 0 .. n+1, one barrier each):
-//   MFMA group (p & 1):       S = QK^T(K_p) if p < n;  O += PV(V_{p-2}, P) if p >= 2
-//   VALU group ((p + 1) & 1): P = softmax(S of tile p-1) if 1 <= p <= n; then it waits
-//                             for the loads it issued two periods ago and issues those
-//                             its own MFMA phase reads in period p+3: K_{p+3} and V_{p+1}.
-// Tile t of K lives in ring slot t & 3 and tile t of V in slot t & 3 (four separate LDS
-// arrays each, so the compiler can tell every load target from every buffer being read
-// and never stalls a read on an unrelated load).  The loads issued at the end of period
-// p overwrite K_{p-1} and V_{p-3}, both last read in period p-1, and are complete and
-// published by the barrier that ends period p+2.  K_0, K_1, K_2 and V_0 are loaded before
-// period 0.  The period loop is unrolled by four so that every slot index is a constant.
-// Afterwards group 1 stores its (m, l, O) in LDS and group 0 merges them into its own
-// (fixed order) and writes the rows.
+// Ping-pong kernel (bf16 sources).  Eight wavefronts in two groups of four alternate an
+// MFMA phase and a VALU phase between workgroup barriers ("periods").  K and V tiles live
+// in a ring of four separate LDS arrays per tensor (slot = tile & 3), so that the compiler
+// can tell each direct-load target from every buffer being read and never stalls a read
+// on an unrelated load; the loops are unrolled by four so every slot index is constant.
+// Loads are issued at the end of a group's VALU phase, after that group waited for the
+// loads it issued in its previous VALU phase; the next barrier publishes them.
+
 template <int P> struct Slot { static constexpr int value = P; };
 
-template <int D, int SRC>
-__global__ __launch_bounds__(NT, 1) void attn_pp_kernel(
-    const int32_t *__restrict__ sched, const qi_tile *__restrict__ tiles, int H,
-    const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
-    __bf16 *__restrict__ o, const uint8_t *__restrict__ cache, float c) {
-  using C = Cfg<D>;
-  __shared__ __attribute__((aligned(1024))) __bf16 K0[C::TILE], K1[C::TILE], K2[C::TILE], K3[C::TILE];
-  __shared__ __attribute__((aligned(1024))) __bf16 V0[C::TILE], V1[C::TILE], V2[C::TILE], V3[C::TILE];
-#define QI_RING(arr, i) ((i) == 0 ? arr##0 : (i) == 1 ? arr##1 : (i) == 2 ? arr##2 : arr##3)
+struct Ring {
+  __bf16 *K0, *K1, *K2, *K3, *V0, *V1, *V2, *V3;
+};
+#define QI_RING(r, arr, i) \
+  ((i) == 0 ? (r).arr##0 : (i) == 1 ? (r).arr##1 : (i) == 2 ? (r).arr##2 : (r).arr##3)
 
-  const int item = sched[blockIdx.x];
-  if (item < 0) return;   // schedule padding
-  const qi_tile tl = tiles[item / H];
-  const int h = item % H;
-  const TileArgs a = make_args(tl, H, h, k, v, cache, false);
+// Row tiles of more than 128 rows: wavefront w owns rows 32w..32w+31 and every key tile
+// is read by all eight wavefronts (group 0 = waves 0..3, group 1 = waves 4..7).
+//   period 2t:   group 0 MFMA phase t: S = QK^T(K_t) (t < n), O += PV(V_{t-1}) (t >= 1)
+//                group 1 VALU phase:  P = softmax(tile t-1); waits; loads its halves of
+//                                     K_{t+2}, V_{t+1} (t >= 1)
+//   period 2t+1: group 1 MFMA phase t; group 0 VALU phase: P = softmax(tile t); waits;
+//                                     loads its halves of K_{t+3}, V_{t+2}
+// Group g loads half g of each tile's rows.  K_0..K_2 and V_0, V_1 are loaded before
+// period 0.  A half tile issued in period p is waited for at the end of p+2 and first read
+// in period >= p+4; the slots it overwrites (K_{m-4}, V_{m-4}) were last read in p-1.
+template <int D, int SRC>
+__device__ __forceinline__ void pp_rows256(const Ring &r, const qi_tile &tl, int H, int h,
+                                           const TileArgs &a, const __bf16 *q, __bf16 *o,
+                                           float c) {
+  using C = Cfg<D>;
   const int wave = threadIdx.x >> 6;
   const int group = wave >> 2;
-  const bool active = (wave & 3) * 32 < tl.nrows;   // the wavefront's rows exist
+  const int row = wave * 32 + (threadIdx.x & 31);
+  const bool active = wave * 32 < tl.nrows;   // the wavefront's rows exist
 
   bf16x8_t qf[C::QS];
-  load_q<D>(q, tl, H, h, qf);
+  load_q<D>(q, tl, H, h, row, qf);
   f32x16_t acc[C::DB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
+    for (int rr = 0; rr < 16; ++rr) acc[db][rr] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
 
   const int n = (tl.kend + BN - 1) / BN;
   Direct<D, SRC> dm;
-  dm.init(a);
-  // prologue: K_0, K_1, K_2 and V_0, each half loaded by one group
-  {
-    __bf16 *dst = group == 0 ? K0 : K1;
-    if (group == 0 || n > 1) dm.issue(group, a, a.k, a.k_off, dst);
-    if (group == 0 && n > 2) dm.issue(2, a, a.k, a.k_off, K2);
-    if (group == 1) dm.issue(0, a, a.v, a.v_off, V0);
+  dm.template issue<1>(0, a, a.k, a.k_off, r.K0, group);
+  if (n > 1) dm.template issue<1>(1, a, a.k, a.k_off, r.K1, group);
+  if (n > 2) dm.template issue<1>(2, a, a.k, a.k_off, r.K2, group);
+  dm.template issue<1>(0, a, a.v, a.v_off, r.V0, group);
+  if (n > 1) dm.template issue<1>(1, a, a.v, a.v_off, r.V1, group);
+  __builtin_amdgcn_s_waitcnt(0);
+  bar();
+
+  f32x16_t s[2];
+  bf16x8_t p[2][2];
+  auto tile = [&](auto slot, int t) {
+    constexpr int T = decltype(slot)::value;   // t & 3
+    auto mfma = [&]() {
+      __builtin_amdgcn_s_setprio(1);
+      if (active) {
+        if (t < n) qk_tile<D>(QI_RING(r, K, T), qf, s);
+        if (t >= 1) pv_tile<D>(QI_RING(r, V, (T + 3) & 3), p, acc);
+      }
+      __builtin_amdgcn_s_setprio(0);
+    };
+    // period 2t
+    if (group == 0) {
+      mfma();
+    } else {
+      if (active && t >= 1 && t <= n) {
+        softmax_max<D>(s, acc, m_run, l_run, t - 1, tl.kend, c);
+        softmax_exp(s, m_run, c, l_run, p);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      if (t >= 1 && t + 2 < n) dm.template issue<1>(t + 2, a, a.k, a.k_off, QI_RING(r, K, (T + 2) & 3), 1);
+      if (t >= 1 && t + 1 < n) dm.template issue<1>(t + 1, a, a.v, a.v_off, QI_RING(r, V, (T + 1) & 3), 1);
+    }
+    bar();
+    // period 2t+1
+    if (group == 1) {
+      mfma();
+    } else {
+      if (active && t < n) {
+        softmax_max<D>(s, acc, m_run, l_run, t, tl.kend, c);
+        softmax_exp(s, m_run, c, l_run, p);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      if (t + 3 < n) dm.template issue<1>(t + 3, a, a.k, a.k_off, QI_RING(r, K, (T + 3) & 3), 0);
+      if (t + 2 < n) dm.template issue<1>(t + 2, a, a.v, a.v_off, QI_RING(r, V, (T + 2) & 3), 0);
+    }
+    bar();
+  };
+  for (int t0 = 0; t0 <= n; t0 += 4) {
+    tile(Slot<0>(), t0);
+    if (t0 + 1 <= n) tile(Slot<1>(), t0 + 1);
+    if (t0 + 2 <= n) tile(Slot<2>(), t0 + 2);
+    if (t0 + 3 <= n) tile(Slot<3>(), t0 + 3);
   }
+  if (active) store_o<D>(o, tl, H, h, row, acc, l_run);
+}
+
+// Row tiles of at most 128 rows: wavefronts w and w+4 hold the same 32 rows and the two
+// groups split the key tiles (tile t belongs to group t & 1).  Period p = 0 .. n+1:
+//   MFMA group (p & 1):       S = QK^T(K_p) if p < n;  O += PV(V_{p-2}, P) if p >= 2
+//   VALU group ((p + 1) & 1): P = softmax(S of tile p-1) if 1 <= p <= n; waits for its
+//                             loads of two periods ago; loads K_{p+3}, V_{p+1} (its own
+//                             MFMA phase reads them in period p+3), overwriting K_{p-1}
+//                             and V_{p-3}, last read in period p-1.
+// K_0, K_1, K_2 and V_0 are loaded before period 0.  Afterwards group 1 stores its
+// (m, l, O) in LDS and group 0 merges them into its own (fixed order).
+template <int D, int SRC>
+__device__ __forceinline__ void pp_rows128(const Ring &r, const qi_tile &tl, int H, int h,
+                                           const TileArgs &a, const __bf16 *q, __bf16 *o,
+                                           float c) {
+  using C = Cfg<D>;
+  const int wave = threadIdx.x >> 6;
+  const int group = wave >> 2;
+  const int row = (wave & 3) * 32 + (threadIdx.x & 31);
+  const bool active = (wave & 3) * 32 < tl.nrows;   // the wavefront's rows exist
+
+  bf16x8_t qf[C::QS];
+  load_q<D>(q, tl, H, h, row, qf);
+  f32x16_t acc[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) acc[db][rr] = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  const int n = (tl.kend + BN - 1) / BN;
+  Direct<D, SRC> dm;
+  if (group == 0) dm.issue(0, a, a.k, a.k_off, r.K0);
+  if (group == 1 && n > 1) dm.issue(1, a, a.k, a.k_off, r.K1);
+  if (group == 0 && n > 2) dm.issue(2, a, a.k, a.k_off, r.K2);
+  if (group == 1) dm.issue(0, a, a.v, a.v_off, r.V0);
   __builtin_amdgcn_s_waitcnt(0);
   bar();
 
@@ -537,8 +620,8 @@ __global__ __launch_bounds__(NT, 1) void attn_pp_kernel(
     if ((P & 1) == group) {
       __builtin_amdgcn_s_setprio(1);
       if (active) {
-        if (per < n) qk_tile<D>(QI_RING(K, P), qf, s);
-        if (per >= 2) pv_tile<D>(QI_RING(V, (P + 2) & 3), p, acc);
+        if (per < n) qk_tile<D>(QI_RING(r, K, P), qf, s);
+        if (per >= 2) pv_tile<D>(QI_RING(r, V, (P + 2) & 3), p, acc);
       }
       __builtin_amdgcn_s_setprio(0);
     } else {
@@ -547,8 +630,8 @@ __global__ __launch_bounds__(NT, 1) void attn_pp_kernel(
         softmax_exp(s, m_run, c, l_run, p);
       }
       __builtin_amdgcn_s_waitcnt(0);   // this group's loads of two periods ago
-      if (per + 3 < n) dm.issue(per + 3, a, a.k, a.k_off, QI_RING(K, (P + 3) & 3));
-      if (per + 1 < n) dm.issue(per + 1, a, a.v, a.v_off, QI_RING(V, (P + 1) & 3));
+      if (per + 3 < n) dm.issue(per + 3, a, a.k, a.k_off, QI_RING(r, K, (P + 3) & 3));
+      if (per + 1 < n) dm.issue(per + 1, a, a.v, a.v_off, QI_RING(r, V, (P + 1) & 3));
     }
     bar();
   };
@@ -558,18 +641,17 @@ __global__ __launch_bounds__(NT, 1) void attn_pp_kernel(
     if (p0 + 2 <= n + 1) period(Slot<2>(), p0 + 2);
     if (p0 + 3 <= n + 1) period(Slot<3>(), p0 + 3);
   }
-#undef QI_RING
 
-  // merge the two partial states of each row (group 1 -> LDS -> group 0); the tile
-  // buffers are free: every load was waited for and every read consumed
+  // merge the two partial states of each row (group 1 -> LDS -> group 0); the ring is
+  // free: every load was waited for and every read consumed
   const int w4 = wave & 3, lane = threadIdx.x & 63;
-  float *ost = reinterpret_cast<float *>(w4 == 0 ? K0 : w4 == 1 ? K1 : w4 == 2 ? K2 : K3) + lane;
-  float *mst = reinterpret_cast<float *>(V0) + (w4 * 64 + lane) * 2;
+  float *ost = reinterpret_cast<float *>(QI_RING(r, K, w4)) + lane;
+  float *mst = reinterpret_cast<float *>(r.V0) + (w4 * 64 + lane) * 2;
   if (group == 1 && active) {
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) ost[(16 * db + r) * 64] = acc[db][r];
+      for (int rr = 0; rr < 16; ++rr) ost[(16 * db + rr) * 64] = acc[db][rr];
     mst[0] = m_run;
     mst[1] = l_run;
   }
@@ -582,11 +664,32 @@ __global__ __launch_bounds__(NT, 1) void attn_pp_kernel(
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[db][r] = acc[db][r] * a0 + ost[(16 * db + r) * 64] * a1;
+      for (int rr = 0; rr < 16; ++rr) acc[db][rr] = acc[db][rr] * a0 + ost[(16 * db + rr) * 64] * a1;
     l_run = l_run * a0 + l1 * a1;
-    store_o<D>(o, tl, H, h, acc, l_run);
+    store_o<D>(o, tl, H, h, row, acc, l_run);
   }
 }
+
+template <int D, int SRC>
+__global__ __launch_bounds__(NT, 1) void attn_pp_kernel(
+    const int32_t *__restrict__ sched, const qi_tile *__restrict__ tiles, int H,
+    const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
+    __bf16 *__restrict__ o, const uint8_t *__restrict__ cache, float c) {
+  using C = Cfg<D>;
+  __shared__ __attribute__((aligned(1024))) __bf16 K0[C::TILE], K1[C::TILE], K2[C::TILE], K3[C::TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 V0[C::TILE], V1[C::TILE], V2[C::TILE], V3[C::TILE];
+  const int item = sched[blockIdx.x];
+  if (item < 0) return;   // schedule padding
+  const qi_tile tl = tiles[item / H];
+  const int h = item % H;
+  const TileArgs a = make_args(tl, H, h, k, v, cache, false);
+  const Ring r{K0, K1, K2, K3, V0, V1, V2, V3};
+  if (tl.nrows > 128)
+    pp_rows256<D, SRC>(r, tl, H, h, a, q, o, c);
+  else
+    pp_rows128<D, SRC>(r, tl, H, h, a, q, o, c);
+}
+#undef QI_RING
 
 // ---------------------------------------------------------------------------------------
 // Register-staged kernel (fp8 cache): plain double-buffered loop.
@@ -603,10 +706,11 @@ __global__ __launch_bounds__(NT_STAGED, 2) void attn_staged_kernel(
   const qi_tile tl = tiles[item / H];
   const int h = item % H;
   const TileArgs a = make_args(tl, H, h, k, v, cache, SRC == SRC_CACHE_FP8);
+  const int row = (threadIdx.x >> 6) * 32 + (threadIdx.x & 31);
   const bool active = (threadIdx.x >> 6) * 32 < tl.nrows;
 
   bf16x8_t qf[C::QS];
-  load_q<D>(q, tl, H, h, qf);
+  load_q<D>(q, tl, H, h, row, qf);
   f32x16_t acc[C::DB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
@@ -635,7 +739,7 @@ __global__ __launch_bounds__(NT_STAGED, 2) void attn_staged_kernel(
     if (j + 2 < n) st.load(j + 2, a);
     __syncthreads();
   }
-  if (active) store_o<D>(o, tl, H, h, acc, l_run);
+  if (active) store_o<D>(o, tl, H, h, row, acc, l_run);
 }
 
 template <int D, int SRC>

@@ -47,56 +47,121 @@ int visible_end(const qi_req_host &r, int row) {
 
 struct Unit {           // all row tiles of one (request, head): they read the same K/V
   int req, head;
-  int64_t cost;         // key tiles processed, summed over the unit's row tiles
+  int64_t cost;         // sum of item costs
   std::vector<int> tiles;
 };
 
-// Deal the (tile, head) items of a call to the XCDs: longest-processing-time-first over
-// units, so that the row tiles sharing a head's K/V stream run on one XCD and share its
-// L2, then interleave the per-XCD lists in launch order (workgroup i goes to XCD i % 8).
-void build_schedule(const qi_plan &p, const std::vector<qi_tile> &tiles,
-                    std::vector<int32_t> &sched) {
+// Cost of one (row tile, head) item: key tiles visited x 128-row blocks.
+int64_t item_cost(const qi_tile &t) {
+  return (int64_t)((t.kend + QI_KERNEL_BN - 1) / QI_KERNEL_BN) * ((t.nrows + 127) / 128);
+}
+
+// Deal the (tile, head) items of a call to the XCDs and order them for launch.
+//  1. Units (request, head) go to XCDs longest-processing-time first, so the row tiles
+//     that stream one head's K/V run on one XCD and share its L2.
+//  2. Per XCD the items are list-scheduled (longest first) on the XCD's workgroup slots.
+//     An item of more than 128 rows whose whole placement would end later than both the
+//     current makespan and the load-balance bound is split into its two 128-row halves
+//     (appended to the tile table); the kernel runs such halves with the key tiles split
+//     over its two wavefront groups, so no slot sits idle at the end of the launch.
+//  3. The per-XCD lists, longest item first, are interleaved in launch order (workgroup i
+//     runs on XCD i % 8).
+void build_schedule(const qi_plan &p, std::vector<qi_tile> &tiles,
+                    const std::vector<std::pair<int, int>> &items_in, int slots_per_xcd,
+                    bool may_split, std::vector<int32_t> &sched) {
   std::vector<Unit> units;
-  std::vector<std::vector<int>> by_req(p.n_req);
-  for (int i = 0; i < (int)tiles.size(); ++i) by_req[tiles[i].req].push_back(i);
-  for (int r = 0; r < p.n_req; ++r) {
-    if (by_req[r].empty()) continue;
-    std::vector<int> order = by_req[r];
-    std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
-      return tiles[a].kend > tiles[b].kend;     // longest row tiles first
-    });
-    int64_t cost = 0;
-    for (int i : order) cost += (tiles[i].kend + QI_KERNEL_BN - 1) / QI_KERNEL_BN;
-    for (int h = 0; h < p.H; ++h) units.push_back(Unit{r, h, cost, order});
+  std::vector<int> unit_of(p.n_req * p.H, -1);
+  for (auto [t, h] : items_in) {
+    int &u = unit_of[tiles[t].req * p.H + h];
+    if (u < 0) {
+      u = (int)units.size();
+      units.push_back(Unit{tiles[t].req, h, 0, {}});
+    }
+    units[u].tiles.push_back(t);
+    units[u].cost += item_cost(tiles[t]);
   }
+  for (Unit &u : units)
+    std::stable_sort(u.tiles.begin(), u.tiles.end(), [&](int a, int b) {
+      return item_cost(tiles[a]) > item_cost(tiles[b]);   // longest row tiles first
+    });
   std::stable_sort(units.begin(), units.end(),
                    [](const Unit &a, const Unit &b) { return a.cost > b.cost; });
-  std::vector<std::vector<int32_t>> bins(QI_NUM_XCD);
+  std::vector<std::vector<std::pair<int, int>>> bins(QI_NUM_XCD);   // (tile, head)
   std::vector<int64_t> load(QI_NUM_XCD, 0);
   for (const Unit &u : units) {
     int best = (int)(std::min_element(load.begin(), load.end()) - load.begin());
     load[best] += u.cost;
-    for (int t : u.tiles) bins[best].push_back(t * p.H + u.head);
+    for (int t : u.tiles) bins[best].push_back({t, u.head});
+  }
+  std::vector<std::vector<int32_t>> lists(QI_NUM_XCD);
+  for (int x = 0; x < QI_NUM_XCD; ++x) {
+    auto &items = bins[x];
+    std::stable_sort(items.begin(), items.end(), [&](const auto &a, const auto &b) {
+      return item_cost(tiles[a.first]) > item_cost(tiles[b.first]);
+    });
+    const int64_t bound = (load[x] + slots_per_xcd - 1) / slots_per_xcd;
+    std::vector<int64_t> slot(slots_per_xcd, 0);
+    int64_t makespan = 0;
+    std::vector<std::pair<int64_t, int32_t>> placed;   // (cost, item code)
+    auto least = [&]() { return (int)(std::min_element(slot.begin(), slot.end()) - slot.begin()); };
+    for (auto [t, h] : items) {
+      const int64_t c = item_cost(tiles[t]);
+      const int s0 = least();
+      bool split = false;
+      if (may_split && tiles[t].nrows > 128 && slot[s0] + c > std::max(makespan, bound)) {
+        const int64_t c1 = c / 2;   // both halves see the same keys
+        std::vector<int64_t> trial = slot;
+        int a = (int)(std::min_element(trial.begin(), trial.end()) - trial.begin());
+        trial[a] += c1;
+        int b = (int)(std::min_element(trial.begin(), trial.end()) - trial.begin());
+        trial[b] += c1;
+        split = std::max(trial[a], trial[b]) < slot[s0] + c;
+      }
+      if (!split) {
+        slot[s0] += c;
+        makespan = std::max(makespan, slot[s0]);
+        placed.push_back({c, t * p.H + h});
+      } else {
+        // new entries for both halves: a tile entry is shared by every head's item
+        qi_tile lo = tiles[t], hi = tiles[t];
+        lo.nrows = 128;
+        hi.q_tok += 128;
+        hi.nrows = tiles[t].nrows - 128;
+        const int t1 = (int)tiles.size();
+        tiles.push_back(lo);
+        tiles.push_back(hi);
+        for (int half : {t1, t1 + 1}) {
+          const int s = least();
+          slot[s] += item_cost(tiles[half]);
+          makespan = std::max(makespan, slot[s]);
+          placed.push_back({item_cost(tiles[half]), half * p.H + h});
+        }
+      }
+    }
+    std::stable_sort(placed.begin(), placed.end(),
+                     [](const auto &a, const auto &b) { return a.first > b.first; });
+    for (auto &pc : placed) lists[x].push_back(pc.second);
   }
   size_t len = 0;
-  for (auto &b : bins) len = std::max(len, b.size());
+  for (auto &l : lists) len = std::max(len, l.size());
   sched.assign(len * QI_NUM_XCD, -1);
-  for (size_t s = 0; s < len; ++s)
+  for (size_t s2 = 0; s2 < len; ++s2)
     for (int x = 0; x < QI_NUM_XCD; ++x)
-      if (s < bins[x].size()) sched[s * QI_NUM_XCD + x] = bins[x][s];
+      if (s2 < lists[x].size()) sched[s2 * QI_NUM_XCD + x] = lists[x][s2];
 }
 
 void build_tiles(const qi_plan &p, int call, std::vector<qi_tile> &tiles) {
   tiles.clear();
+  const int bm = p.bm[call];
   std::vector<std::pair<int, int>> blocks;
   for (int r = 0; r < p.n_req; ++r) {
     const qi_req_host &rq = p.req[r];
     int nkeys = 0;
     call_blocks(rq, call, blocks, nkeys);
     for (auto [start, len] : blocks) {
-      for (int r0 = start; r0 < start + len; r0 += QI_KERNEL_BM) {
+      for (int r0 = start; r0 < start + len; r0 += bm) {
         qi_tile t{};
-        t.nrows = std::min(QI_KERNEL_BM, start + len - r0);
+        t.nrows = std::min(bm, start + len - r0);
         t.kend = std::min(visible_end(rq, r0), nkeys);
         t.req = r;
         t.k_off = rq.k_off;
@@ -230,12 +295,51 @@ qi_status qi_plan_create(const qi_wave_desc *d, qi_plan **out) {
   }
   std::vector<qi_tile> tiles[3];
   std::vector<int32_t> sched[3];
+  // prefix and denoising calls: row tiles per block, balanced (and split) per call.  The
+  // full call reuses exactly their decomposition, (row tile, head) by (row tile, head),
+  // so every row runs the same kernel path over the same key tiles in every call and the
+  // results agree bit for bit (reuse is exact).
+  for (int c : {QI_CALL_PREFIX, QI_CALL_DENOISE}) {
+    p->bm[c] = (c == QI_CALL_DENOISE && p->kv == QI_KV_FP8_E4M3) ? QI_ROWS_FP8 : QI_ROWS_BF16;
+    build_tiles(*p, c, tiles[c]);
+    std::vector<std::pair<int, int>> items;
+    for (int t = 0; t < (int)tiles[c].size(); ++t)
+      for (int h = 0; h < p->H; ++h) items.push_back({t, h});
+    // the bf16-source kernel runs one 8-wavefront workgroup per CU; the fp8 one two
+    // 4-wavefront workgroups
+    const bool fp8 = p->bm[c] == QI_ROWS_FP8;
+    build_schedule(*p, tiles[c], items, QI_CUS_PER_XCD * (fp8 ? 2 : 1), !fp8, sched[c]);
+  }
+  {
+    p->bm[QI_CALL_FULL] = QI_ROWS_BF16;
+    std::vector<std::pair<int, int>> items;
+    std::vector<qi_tile> &ft = tiles[QI_CALL_FULL];
+    for (int c : {QI_CALL_PREFIX, QI_CALL_DENOISE}) {
+      std::vector<int> map(tiles[c].size(), -1);
+      for (int32_t code : sched[c]) {
+        if (code < 0) continue;
+        const int t = code / p->H, h = code % p->H;
+        if (map[t] < 0) {
+          const qi_tile &src = tiles[c][t];
+          const qi_req_host &rq = p->req[src.req];
+          const int r0 = c == QI_CALL_PREFIX ? src.q_tok - rq.pre_tok
+                                             : src.q_tok - rq.img_tok + rq.lp;
+          qi_tile f = src;
+          f.q_tok = rq.all_tok + r0;
+          f.kv_tok = rq.all_tok;
+          f.lp = 0;
+          map[t] = (int)ft.size();
+          ft.push_back(f);
+        }
+        items.push_back({map[t], h});
+      }
+    }
+    build_schedule(*p, ft, items, QI_CUS_PER_XCD, false, sched[QI_CALL_FULL]);
+  }
   size_t off = 0;
   p->reqs_off = off;
   off = align_up(off + reqs.size() * sizeof(qi_req_dev));
   for (int c = 0; c < 3; ++c) {
-    build_tiles(*p, c, tiles[c]);
-    build_schedule(*p, tiles[c], sched[c]);
     p->n_tiles[c] = (int32_t)tiles[c].size();
     p->sched_len[c] = (int32_t)sched[c].size();
     p->tiles_off[c] = off;
@@ -266,9 +370,9 @@ qi_status qi_plan_sizes(const qi_plan *p, size_t *cache_bytes, size_t *workspace
   return QI_OK;
 }
 
-qi_status qi_plan_kernel_tile(const qi_plan *p, int32_t *bm, int32_t *bn) {
-  if (!p || !bm || !bn) return QI_ERR_INVALID_ARG;
-  *bm = QI_KERNEL_BM;
+qi_status qi_plan_kernel_tile(const qi_plan *p, int32_t call, int32_t *bm, int32_t *bn) {
+  if (!p || !bm || !bn || call < 0 || call > 2) return QI_ERR_INVALID_ARG;
+  *bm = p->bm[call];
   *bn = QI_KERNEL_BN;
   return QI_OK;
 }

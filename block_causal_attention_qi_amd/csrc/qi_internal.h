@@ -9,18 +9,23 @@
 
 #include "qi.h"   // include/ of the repository, on the include path
 
-// Attention tile: rows per workgroup (4 x 32 query rows; the ping-pong kernel splits keys over two groups) x keys per step.
-#define QI_KERNEL_BM 128
+// Attention tiles: rows per workgroup x keys per step.  bf16 key sources run row tiles of
+// up to 256 rows (8 wavefronts x 32 rows; tiles of <= 128 rows split their keys over two
+// wave groups); the fp8-cache kernel runs 128-row tiles (4 wavefronts x 32 rows).
+#define QI_ROWS_BF16 256
+#define QI_ROWS_FP8 128
 #define QI_KERNEL_BN 64
-// Number of XCDs of the MI355X; workgroups are dealt to them round-robin in launch order.
+// Number of XCDs of the MI355X and compute units per XCD; workgroups are dealt to the XCDs
+// round-robin in launch order.
 #define QI_NUM_XCD 8
+#define QI_CUS_PER_XCD 32
 // Prefix tokens per workgroup in the cache-write kernels.
 #define QI_CACHE_CHUNK 64
 
 // One row tile of one request for one call (device table entry, 48 bytes).
 struct qi_tile {
   int32_t q_tok;      // packed token index (in the call's Q and O tensors) of the first row
-  int32_t nrows;      // 1 .. QI_KERNEL_BM
+  int32_t nrows;      // 1 .. row tile size of the call
   int32_t kend;       // attended keys are positions [0, kend) of the request
   int32_t kv_tok;     // packed token index (in the call's live K/V) of key position `lp`
   int32_t lp;         // keys below lp come from the prefix cache (denoise); else 0
@@ -62,6 +67,7 @@ struct qi_plan {
   size_t ws_bytes = 0;
   size_t tiles_off[3] = {0, 0, 0}, sched_off[3] = {0, 0, 0};
   int32_t n_tiles[3] = {0, 0, 0}, sched_len[3] = {0, 0, 0};
+  int32_t bm[3] = {0, 0, 0};   // row tile size per call
   size_t reqs_off = 0, part_off = 0, part_floats = 0;
   int32_t max_chunks = 0;
 

@@ -59,7 +59,7 @@ def _load():
         "qi_denoise_attn_step": ([P, VP, SZ, VP, VP, VP, VP, VP], I32),
         "qi_attn_full_reference_step": ([P, VP, VP, VP, VP, VP], I32),
         "qi_plan_tile_map": ([P, I32, I32, I32, VP, SZ, ctypes.POINTER(SZ)], I32),
-        "qi_plan_kernel_tile": ([P, ctypes.POINTER(I32), ctypes.POINTER(I32)], I32),
+        "qi_plan_kernel_tile": ([P, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)], I32),
         "qi_plan_cache_offset": ([P, I32, I32, I32, I32, ctypes.POINTER(SZ)], I32),
         "qi_plan_pairs": ([P, I32, ctypes.POINTER(I64)], I32),
         "qi_plan_tokens": ([P, ctypes.POINTER(I64), ctypes.POINTER(I64), ctypes.POINTER(I64)], I32),
@@ -230,9 +230,9 @@ def qi_plan_tile_map(plan, call, bm, bn):
     return out[:need.value]
 
 
-def qi_plan_kernel_tile(plan):
+def qi_plan_kernel_tile(plan, call):
     bm, bn = ctypes.c_int32(), ctypes.c_int32()
-    _check(lib.qi_plan_kernel_tile(plan.handle, ctypes.byref(bm), ctypes.byref(bn)),
+    _check(lib.qi_plan_kernel_tile(plan.handle, call, ctypes.byref(bm), ctypes.byref(bn)),
            "qi_plan_kernel_tile")
     return bm.value, bn.value
 

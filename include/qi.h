@@ -146,9 +146,10 @@ qi_status qi_attn_full_reference_step(const qi_plan *plan, const void *q_all,
 qi_status qi_plan_tile_map(const qi_plan *plan, int32_t call, int32_t bm, int32_t bn,
                            uint8_t *host_out, size_t n, size_t *n_needed);
 
-/* Tile shape (rows x keys) the attention kernels use; the tile map for this shape is the
- * one the kernels follow. */
-qi_status qi_plan_kernel_tile(const qi_plan *plan, int32_t *bm, int32_t *bn);
+/* Tile shape (rows x keys) the attention kernel of a call uses; the tile map of the call
+ * for this shape is the one the kernel follows (row tiles of the bf16-source kernel with
+ * at most 128 rows additionally split their key tiles over two wavefront groups). */
+qi_status qi_plan_kernel_tile(const qi_plan *plan, int32_t call, int32_t *bm, int32_t *bn);
 
 /* Byte offset in the cache arena of element (request, kv = 0 K | 1 V, head, token,
  * channel 0); for kv = 2 the offset of the request's float32 scales [2][H] (fp8 only). */

@@ -46,7 +46,7 @@ def test_tile_maps_match_oracle(reqs, h, d):
     for kv in ("bf16", "fp8"):
         p = qi.Plan(reqs, h, d, kv)
         for call in (qi.QI_CALL_PREFIX, qi.QI_CALL_DENOISE, qi.QI_CALL_FULL):
-            tilings = [qi.qi_plan_kernel_tile(p), (64, 64), (128, 128)]
+            tilings = [qi.qi_plan_kernel_tile(p, call), (64, 64), (128, 128), (256, 64)]
             if sum(map(sum, reqs)) < 3000:
                 tilings += [(3, 5), (16, 32), (1, 1)]
             for bm, bn in tilings:

@@ -117,7 +117,7 @@ def big():
 def _sampled(gw, e, call, out, kv, n_random, seed, bar):
     w = gw.w
     rng = np.random.default_rng(seed)
-    bm, _ = qi.qi_plan_kernel_tile(gw.plan)
+    bm, _ = qi.qi_plan_kernel_tile(gw.plan, call)
     heads = sorted({0, w.n_heads - 1} | set(int(h) for h in rng.integers(0, w.n_heads, 4)))
     rows = [sample_rows(bl, call, bm, rng, n_random) for bl in w.requests]
     ref = oracle_rows(w, call, e, rows, kv, heads)
