@@ -74,16 +74,28 @@ struct Cfg {
   static constexpr int PASS = BN / ROWS;        // passes per tile
   static constexpr int QS = D / 16;          // MFMA k-steps over the head dim
   static constexpr int DB = D / 32;          // 32-wide blocks of the output
-  static constexpr int TILE = BN * D;        // bf16 elements per staged K (or V) tile
-  static constexpr int IPW = D / 32;         // 1 KiB direct loads per wavefront per tile
-  static constexpr int RPK = 512 / D;        // rows per 1 KiB
+  static constexpr int IPW = D / 32;         // 1 KiB direct V loads per wavefront per tile
+  static constexpr int RPK = 512 / D;        // V rows per 1 KiB
   static_assert(PASS * ROWS == BN && IPW * RPK * 4 == BN, "tile shape");
-  // Physical 16-byte chunk = logical chunk ^ swz(row).  One swizzle serves both tiles:
-  //  K reads: 16 lanes read one chunk of 16 consecutive rows -> 16 distinct bank groups;
-  //  V transpose reads: 32 lanes read 64 bytes of 4 consecutive rows -> 64 distinct banks.
-  __device__ static constexpr int swz(int r) {
-    return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+  // K tile: two halves of 32 rows; a row takes 2D bytes plus one spare 16-byte slot, so
+  // 16 consecutive rows start in 16 distinct bank groups (2D + 16 = 16 mod 256 for D=128,
+  // 144 for D=64; both generate all 16 slots) and a lane reads all of its row's chunks at
+  // one base address plus constant offsets.
+  static constexpr int KSTRIDE = 2 * D + 16;             // bytes per K row
+  static constexpr int KCH = KSTRIDE / 16;               // 16-byte slots per K row
+  static constexpr int KHALF_N = (32 * KCH + 63) / 64;   // 1 KiB loads per half
+  static constexpr int KHALF = KHALF_N * 1024;           // bytes per half
+  static constexpr int KTILE = KHALF;                    // bf16 elements per K tile (2 halves)
+  static constexpr int VTILE = BN * D;                   // bf16 elements per V tile
+  // V tile: rows of 2D bytes; the 64-byte quarter q of row r sits at quarter q ^ vq(r), so
+  // the transpose reads (32 lanes: 64 bytes of one quarter in each of 4 consecutive rows)
+  // hit 64 distinct banks and a lane needs one base address per quarter.
+  __device__ static constexpr int vq(int r) { return D == 128 ? (r & 3) : ((r >> 1) & 1); }
+  // byte offsets of 16-byte chunk c of row r
+  __device__ static constexpr int koff(int r, int c) {
+    return (r >> 5) * KHALF + (r & 31) * KSTRIDE + c * 16;
   }
+  __device__ static constexpr int voff(int r, int c) { return r * 2 * D + ((c ^ (vq(r) << 2)) << 4); }
 };
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
@@ -136,66 +148,110 @@ __device__ __forceinline__ int tile_kind(int kt, const TileArgs &a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Direct global -> LDS tile loads (bf16 sources).  A tile is 64 x D bf16, i.e. 16 (D=128)
-// or 8 (D=64) KiB; the four wavefronts of one group each fill consecutive KiB of it (all
-// of it, or one half).  In KiB `kib` lane l writes the 16 bytes at offset 16 l: row
-// kib * RPK + l / CH, physical chunk l % CH, so it loads logical chunk (l % CH) ^ swz(row)
-// of that key row.
-template <int D, int SRC>
+// Direct global -> LDS tile loads (bf16 sources).  Every load instruction fills 1 KiB of
+// LDS, lane l the 16 bytes at offset 16 l, so the layout is set on the global side: each
+// lane fetches the key row and chunk that belongs at its LDS slot.
+//   K: instruction i of half hf covers slots 64 i + l of that half; slot s holds row
+//      32 hf + s / KCH, chunk s % KCH; the spare slot of a row and the slots past the 32
+//      rows of a half take a copy of a real chunk of the half (never read).
+//   V: KiB kib holds rows kib * RPK + l / CH; physical chunk p of row r is logical chunk
+//      p ^ (vq(r) << 2) (vq depends on l only, as kib * RPK is a multiple of 4).
+// A group of four wavefronts loads either whole tiles (HALF = false) or one half of the
+// rows of each tile (HALF = true, the other group loads the other half); wavefront w of
+// the group issues the K instructions w, w + 4, ... and a run of consecutive V
+// instructions.  Instruction indices are wavefront-uniform, so the LDS destination is a
+// scalar; the per-lane part of every global address is a 32-bit offset computed once,
+// added to a scalar base per tile.  Key tiles that straddle the cache/live boundary or
+// kend take a slower per-lane path.
+template <int D, int SRC, bool HALF>
 struct Direct {
   using C = Cfg<D>;
-  __device__ __forceinline__ void init(const TileArgs &) {}
+  static constexpr int NIK = HALF ? C::KHALF_N : 2 * C::KHALF_N;   // K instructions loaded
+  static constexpr int NIV = HALF ? 2 * C::IPW : 4 * C::IPW;       // V instructions loaded
+  static constexpr int UK = (NIK + 3) / 4;                          // per wavefront, at most
+  static constexpr int UV = NIV / 4;                                // per wavefront
+  int w;                                  // wavefront index in the group (uniform)
+  uint32_t krow[UK], kch[UK];             // K: row in the tile (or half) and chunk, per load
+  uint32_t v_live, v_cache;               // V: lane offset from the instruction's first row
 
-  // lane l of the wavefront writes the 16 bytes at offset 16 l of KiB `kib` of the tile
-  __device__ __forceinline__ static void dma(const __bf16 *src, __bf16 *tile, int kib) {
-    __builtin_amdgcn_global_load_lds(src, (lds_void_t *)(tile + kib * 512), 16, 0, 0);
+  __device__ __forceinline__ void init(const TileArgs &a) {
+    w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 3;
+    const int l = threadIdx.x & 63;
+#pragma unroll
+    for (int u = 0; u < UK; ++u) {
+      const int j = 4 * u + w;
+      const int hf = HALF ? 0 : j / C::KHALF_N, i = HALF ? j : j % C::KHALF_N;
+      const int sl = 64 * i + l;
+      krow[u] = 32 * hf + min(sl / C::KCH, 31);
+      kch[u] = min(sl % C::KCH, C::CH - 1);
+    }
+    const int vr = l / C::CH, vc = (l % C::CH) ^ (C::vq(vr) << 2);
+    v_live = (uint32_t)(vr * a.H * D + vc * 8) * 2u;
+    v_cache = (uint32_t)(vr * D + vc * 8) * 2u;
   }
 
-  // issue the loads of tile kt of one tensor (K: live = a.k, coff = a.k_off).  HALF < 0:
-  // the four wavefronts of the calling group load the whole tile; HALF = 0 / 1: they load
-  // the first / second half of its rows (the other group loads the rest).
-  template <int HALF = -1>
+  __device__ __forceinline__ static void load(const char *src, __bf16 *tile, int dst) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void_t *)(reinterpret_cast<char *>(tile) + dst), 16,
+                                     0, 0);
+  }
+
+  // key row `key` of this (request, head): cache below lp, else live
+  __device__ __forceinline__ static const char *row_ptr(const TileArgs &a, const __bf16 *live,
+                                                        int64_t coff, int key) {
+    if (SRC != SRC_ONE && key < a.lp)
+      return reinterpret_cast<const char *>(a.cache + coff) + (int64_t)(a.h * a.lp + key) * D * 2;
+    return reinterpret_cast<const char *>(live + ((int64_t)(a.kv_tok + key - a.lp) * a.H + a.h) * D);
+  }
+
+  // loads of tile kt of K (IS_K; live = a.k, coff = a.k_off) or V; HALF: rows of half hf
+  template <bool IS_K>
   __device__ __forceinline__ void issue(int kt, const TileArgs &a, const __bf16 *live,
-                                        int64_t coff, __bf16 *tile, int half = 0) const {
-    constexpr int N = HALF < 0 ? C::IPW : C::IPW / 2;
-    const int i0 = HALF < 0 ? 0 : half * (C::IPW / 2) * 4;   // first KiB index offset
-    const int k0 = kt * BN;
+                                        int64_t coff, __bf16 *tile, int hf = 0) const {
+    const int k0 = kt * BN + (HALF ? 32 * hf : 0);   // first key of the loaded rows
     const int kd = tile_kind<SRC>(kt, a);
-    if (kd == LIVE) {
-      const __bf16 *base = live + ((int64_t)(a.kv_tok + k0 - a.lp) * a.H + a.h) * D;
+    if (kd == LIVE || (SRC != SRC_ONE && kd == CACHED)) {
+      const bool lv = kd == LIVE;
+      const char *base = row_ptr(a, live, coff, k0);     // uniform
+      const uint32_t rstride = lv ? a.H * D * 2 : D * 2;   // bytes between key rows
+      if (IS_K) {
 #pragma unroll
-      for (int i = 0; i < N; ++i) dma_at(base, tile, i0, i, N, true, a);
-    } else if (SRC != SRC_ONE && kd == CACHED) {
-      const __bf16 *base =
-          reinterpret_cast<const __bf16 *>(a.cache + coff) + (int64_t)(a.h * a.lp + k0) * D;
+        for (int u = 0; u < UK; ++u) {
+          const int j = 4 * u + w;
+          if (NIK % 4 != 0 && j >= NIK) break;
+          const int dst = (HALF ? hf * C::KHALF : (j / C::KHALF_N) * C::KHALF) + (j % C::KHALF_N) * 1024;
+          load(base + (krow[u] * rstride + kch[u] * 16), tile, dst);
+        }
+      } else {
 #pragma unroll
-      for (int i = 0; i < N; ++i) dma_at(base, tile, i0, i, N, false, a);
+        for (int u = 0; u < UV; ++u) {
+          const int ins = UV * w + u;   // V instruction within the loaded rows
+          const int dst = (HALF ? hf * (NIV * 1024) : 0) + ins * 1024;
+          load(base + (uint32_t)(ins * C::RPK) * rstride + (lv ? v_live : v_cache), tile, dst);
+        }
+      }
     } else {
+      // mixed sources or rows past kend (those load key kend - 1: finite values of this
+      // request, masked later)
+      const int l = threadIdx.x & 63;
 #pragma unroll
-      for (int i = 0; i < N; ++i) {
-        const int kib = i0 + (threadIdx.x >> 6 & 3) * N + i;
-        const int row = kib * C::RPK + (threadIdx.x & 63) / C::CH;
-        const int chunk = ((threadIdx.x & 63) % C::CH) ^ C::swz(row);
-        // keys past kend load key kend - 1: finite values of this request, masked later
-        const int key = min(k0 + row, a.kend - 1);
-        const __bf16 *src;
-        if (SRC != SRC_ONE && key < a.lp)
-          src = reinterpret_cast<const __bf16 *>(a.cache + coff) + (int64_t)(a.h * a.lp + key) * D;
-        else
-          src = live + ((int64_t)(a.kv_tok + key - a.lp) * a.H + a.h) * D;
-        dma(src + chunk * 8, tile, kib);
+      for (int u = 0; u < (IS_K ? UK : UV); ++u) {
+        int r, ch, dst;
+        if (IS_K) {
+          const int j = 4 * u + w;
+          if (NIK % 4 != 0 && j >= NIK) break;
+          r = krow[u];
+          ch = kch[u];
+          dst = (HALF ? hf * C::KHALF : (j / C::KHALF_N) * C::KHALF) + (j % C::KHALF_N) * 1024;
+        } else {
+          const int ins = UV * w + u;
+          r = ins * C::RPK + l / C::CH;
+          ch = (l % C::CH) ^ (C::vq(r) << 2);
+          dst = (HALF ? hf * (NIV * 1024) : 0) + ins * 1024;
+        }
+        const int key = min(k0 + r, a.kend - 1);
+        load(row_ptr(a, live, coff, key) + ch * 16, tile, dst);
       }
     }
-  }
-
-  // KiB kib = i0 + (wave % 4) * N + i of the tile, from a whole-tile base pointer
-  __device__ __forceinline__ static void dma_at(const __bf16 *base, __bf16 *tile, int i0, int i,
-                                                int N, bool live, const TileArgs &a) {
-    const int kib = i0 + (threadIdx.x >> 6 & 3) * N + i;
-    const int row = kib * C::RPK + (threadIdx.x & 63) / C::CH;
-    const int chunk = ((threadIdx.x & 63) % C::CH) ^ C::swz(row);
-    const int off = live ? row * a.H * D + chunk * 8 : row * D + chunk * 8;
-    dma(base + off, tile, kib);
   }
 };
 
@@ -275,8 +331,8 @@ struct Stage {
         kv = dequant8(kv.x, kv.y, a.k_scale);
         vv = dequant8(vv.x, vv.y, a.v_scale);
       }
-      *reinterpret_cast<uint4 *>(Ks + r * D + ((chunk ^ C::swz(r)) << 3)) = kv;
-      *reinterpret_cast<uint4 *>(Vs + r * D + ((chunk ^ C::swz(r)) << 3)) = vv;
+      *reinterpret_cast<uint4 *>(reinterpret_cast<char *>(Ks) + C::koff(r, chunk)) = kv;
+      *reinterpret_cast<uint4 *>(reinterpret_cast<char *>(Vs) + C::voff(r, chunk)) = vv;
     }
   }
 };
@@ -296,6 +352,8 @@ __device__ __forceinline__ void qk_tile(const __bf16 *Ks, const bf16x8_t (&qf)[C
   using C = Cfg<D>;
   const int lane = threadIdx.x & 63;
   const int j = lane & 31, g = lane >> 5;
+  // row j (+32 kb) of the tile, chunk 2 st + g
+  const char *kp = reinterpret_cast<const char *>(Ks) + C::koff(j, g);
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -304,10 +362,8 @@ __device__ __forceinline__ void qk_tile(const __bf16 *Ks, const bf16x8_t (&qf)[C
   for (int st = 0; st < C::QS; ++st) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const int row = kb * 32 + j;
-      const int ch = 2 * st + g;
       const bf16x8_t a =
-          *reinterpret_cast<const bf16x8_t *>(Ks + row * D + ((ch ^ C::swz(row)) << 3));
+          *reinterpret_cast<const bf16x8_t *>(kp + kb * C::KHALF + st * 32);
       s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s[kb], 0, 0, 0);
     }
   }
@@ -350,10 +406,10 @@ __device__ __forceinline__ void softmax_max(f32x16_t (&s)[2], f32x16_t (&o)[Cfg<
 
 // P = 2^(s c - m) in bf16, in the MFMA B-operand order: step (kb, cc) holds keys
 // 32kb + 16cc + {4g..4g+3, 8+4g..8+4g+3}, i.e. this lane's score registers 8cc..8cc+7.
-// The row sum accumulates the same bf16 values the PV product uses.
+// The row sum accumulates the fp32 values before rounding (plain adds: they overlap the
+// other wavefront's MFMAs, which v_dot2 does not).
 __device__ __forceinline__ void softmax_exp(const f32x16_t (&s)[2], float m_run, float c,
                                             float &l_run, bf16x8_t (&p)[2][2]) {
-  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -364,8 +420,7 @@ __device__ __forceinline__ void softmax_exp(const f32x16_t (&s)[2], float m_run,
         const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * cc + 2 * t], c, -m_run));
         const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * cc + 2 * t + 1], c, -m_run));
         w[t] = pack_bf16(x0, x1);
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[t]), ones, l_run,
-                                                false);
+        l_run += x0 + x1;
       }
       uint4 u = make_uint4(w[0], w[1], w[2], w[3]);
       p[kb][cc] = __builtin_bit_cast(bf16x8_t, u);
@@ -383,8 +438,13 @@ __device__ __forceinline__ void pv_tile(const __bf16 *Vs, const bf16x8_t (&p)[2]
   const int lane = threadIdx.x & 63;
   const int g = lane >> 5;
   const int i16 = lane & 15;
-  const int rsub = i16 >> 2;
-  const int dsub = 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);
+  // this lane's first row and its 8 bytes inside the dims of each 32-dim block
+  const int r0 = 4 * g + (i16 >> 2);
+  const int c2 = 2 * ((lane >> 4) & 1) + ((i16 & 3) >> 1);
+  const char *vp[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+    vp[db] = reinterpret_cast<const char *>(Vs) + C::voff(r0, 4 * db + c2) + 8 * (i16 & 1);
   // the four output blocks are independent accumulation chains: interleave them so that
   // consecutive MFMAs never wait on each other's results
 #pragma unroll
@@ -393,12 +453,11 @@ __device__ __forceinline__ void pv_tile(const __bf16 *Vs, const bf16x8_t (&p)[2]
     for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) {
-        const int dim = db * 32 + dsub;
         i16x4_t h[2];
 #pragma unroll
         for (int r8 = 0; r8 < 2; ++r8) {
-          const int row = 32 * kb + 16 * cc + 8 * r8 + 4 * g + rsub;
-          const __bf16 *src = Vs + row * D + (((dim >> 3) ^ C::swz(row)) << 3) + (dim & 7);
+          // rows r0 + 32 kb + 16 cc + 8 r8 share the quarter placement of row r0
+          const char *src = vp[db] + (32 * kb + 16 * cc + 8 * r8) * 2 * D;
           h[r8] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(src));
         }
         const i16x8_t both = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
@@ -519,12 +578,13 @@ __device__ __forceinline__ void pp_rows256(const Ring &r, const qi_tile &tl, int
   float m_run = -INFINITY, l_run = 0.0f;
 
   const int n = (tl.kend + BN - 1) / BN;
-  Direct<D, SRC> dm;
-  dm.template issue<1>(0, a, a.k, a.k_off, r.K0, group);
-  if (n > 1) dm.template issue<1>(1, a, a.k, a.k_off, r.K1, group);
-  if (n > 2) dm.template issue<1>(2, a, a.k, a.k_off, r.K2, group);
-  dm.template issue<1>(0, a, a.v, a.v_off, r.V0, group);
-  if (n > 1) dm.template issue<1>(1, a, a.v, a.v_off, r.V1, group);
+  Direct<D, SRC, true> dm;
+  dm.init(a);
+  dm.template issue<true>(0, a, a.k, a.k_off, r.K0, group);
+  if (n > 1) dm.template issue<true>(1, a, a.k, a.k_off, r.K1, group);
+  if (n > 2) dm.template issue<true>(2, a, a.k, a.k_off, r.K2, group);
+  dm.template issue<false>(0, a, a.v, a.v_off, r.V0, group);
+  if (n > 1) dm.template issue<false>(1, a, a.v, a.v_off, r.V1, group);
   __builtin_amdgcn_s_waitcnt(0);
   bar();
 
@@ -549,8 +609,8 @@ __device__ __forceinline__ void pp_rows256(const Ring &r, const qi_tile &tl, int
         softmax_exp(s, m_run, c, l_run, p);
       }
       __builtin_amdgcn_s_waitcnt(0);
-      if (t >= 1 && t + 2 < n) dm.template issue<1>(t + 2, a, a.k, a.k_off, QI_RING(r, K, (T + 2) & 3), 1);
-      if (t >= 1 && t + 1 < n) dm.template issue<1>(t + 1, a, a.v, a.v_off, QI_RING(r, V, (T + 1) & 3), 1);
+      if (t >= 1 && t + 2 < n) dm.template issue<true>(t + 2, a, a.k, a.k_off, QI_RING(r, K, (T + 2) & 3), 1);
+      if (t >= 1 && t + 1 < n) dm.template issue<false>(t + 1, a, a.v, a.v_off, QI_RING(r, V, (T + 1) & 3), 1);
     }
     bar();
     // period 2t+1
@@ -562,8 +622,8 @@ __device__ __forceinline__ void pp_rows256(const Ring &r, const qi_tile &tl, int
         softmax_exp(s, m_run, c, l_run, p);
       }
       __builtin_amdgcn_s_waitcnt(0);
-      if (t + 3 < n) dm.template issue<1>(t + 3, a, a.k, a.k_off, QI_RING(r, K, (T + 3) & 3), 0);
-      if (t + 2 < n) dm.template issue<1>(t + 2, a, a.v, a.v_off, QI_RING(r, V, (T + 2) & 3), 0);
+      if (t + 3 < n) dm.template issue<true>(t + 3, a, a.k, a.k_off, QI_RING(r, K, (T + 3) & 3), 0);
+      if (t + 2 < n) dm.template issue<false>(t + 2, a, a.v, a.v_off, QI_RING(r, V, (T + 2) & 3), 0);
     }
     bar();
   };
@@ -605,11 +665,12 @@ __device__ __forceinline__ void pp_rows128(const Ring &r, const qi_tile &tl, int
   float m_run = -INFINITY, l_run = 0.0f;
 
   const int n = (tl.kend + BN - 1) / BN;
-  Direct<D, SRC> dm;
-  if (group == 0) dm.issue(0, a, a.k, a.k_off, r.K0);
-  if (group == 1 && n > 1) dm.issue(1, a, a.k, a.k_off, r.K1);
-  if (group == 0 && n > 2) dm.issue(2, a, a.k, a.k_off, r.K2);
-  if (group == 1) dm.issue(0, a, a.v, a.v_off, r.V0);
+  Direct<D, SRC, false> dm;
+  dm.init(a);
+  if (group == 0) dm.template issue<true>(0, a, a.k, a.k_off, r.K0);
+  if (group == 1 && n > 1) dm.template issue<true>(1, a, a.k, a.k_off, r.K1);
+  if (group == 0 && n > 2) dm.template issue<true>(2, a, a.k, a.k_off, r.K2);
+  if (group == 1) dm.template issue<false>(0, a, a.v, a.v_off, r.V0);
   __builtin_amdgcn_s_waitcnt(0);
   bar();
 
@@ -630,8 +691,8 @@ __device__ __forceinline__ void pp_rows128(const Ring &r, const qi_tile &tl, int
         softmax_exp(s, m_run, c, l_run, p);
       }
       __builtin_amdgcn_s_waitcnt(0);   // this group's loads of two periods ago
-      if (per + 3 < n) dm.issue(per + 3, a, a.k, a.k_off, QI_RING(r, K, (P + 3) & 3));
-      if (per + 1 < n) dm.issue(per + 1, a, a.v, a.v_off, QI_RING(r, V, (P + 1) & 3));
+      if (per + 3 < n) dm.template issue<true>(per + 3, a, a.k, a.k_off, QI_RING(r, K, (P + 3) & 3));
+      if (per + 1 < n) dm.template issue<false>(per + 1, a, a.v, a.v_off, QI_RING(r, V, (P + 1) & 3));
     }
     bar();
   };
@@ -676,8 +737,8 @@ __global__ __launch_bounds__(NT, 1) void attn_pp_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     __bf16 *__restrict__ o, const uint8_t *__restrict__ cache, float c) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(1024))) __bf16 K0[C::TILE], K1[C::TILE], K2[C::TILE], K3[C::TILE];
-  __shared__ __attribute__((aligned(1024))) __bf16 V0[C::TILE], V1[C::TILE], V2[C::TILE], V3[C::TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 K0[C::KTILE], K1[C::KTILE], K2[C::KTILE], K3[C::KTILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 V0[C::VTILE], V1[C::VTILE], V2[C::VTILE], V3[C::VTILE];
   const int item = sched[blockIdx.x];
   if (item < 0) return;   // schedule padding
   const qi_tile tl = tiles[item / H];
@@ -699,7 +760,7 @@ __global__ __launch_bounds__(NT_STAGED, 2) void attn_staged_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     __bf16 *__restrict__ o, const uint8_t *__restrict__ cache, float c) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(1024))) __bf16 lds[2][2 * C::TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 lds[2][C::KTILE + C::VTILE];
 
   const int item = sched[blockIdx.x];
   if (item < 0) return;
@@ -722,7 +783,7 @@ __global__ __launch_bounds__(NT_STAGED, 2) void attn_staged_kernel(
   Stage<D, SRC> st;
   st.init(a);
   st.load(0, a);
-  st.store(0, a, lds[0], lds[0] + C::TILE);
+  st.store(0, a, lds[0], lds[0] + C::KTILE);
   if (n > 1) st.load(1, a);
   __syncthreads();
   for (int j = 0; j < n; ++j) {
@@ -733,9 +794,9 @@ __global__ __launch_bounds__(NT_STAGED, 2) void attn_staged_kernel(
       qk_tile<D>(lds[cur], qf, s);
       softmax_max<D>(s, acc, m_run, l_run, j, tl.kend, c);
       softmax_exp(s, m_run, c, l_run, p);
-      pv_tile<D>(lds[cur] + C::TILE, p, acc);
+      pv_tile<D>(lds[cur] + C::KTILE, p, acc);
     }
-    if (j + 1 < n) st.store(j + 1, a, lds[cur ^ 1], lds[cur ^ 1] + C::TILE);
+    if (j + 1 < n) st.store(j + 1, a, lds[cur ^ 1], lds[cur ^ 1] + C::KTILE);
     if (j + 2 < n) st.load(j + 2, a);
     __syncthreads();
   }
