@@ -10,16 +10,17 @@
 // [H][L_p][D], V [H][L_p][D], head-major so that each (request, head) key stream is one
 // contiguous run for the attention kernel's tile loads.
 //
-// bf16 cache: one pass, a re-layout copy (16 bytes per lane, coalesced reads and writes).
+// bf16 cache: one pass, a re-layout copy (16 bytes per lane, contiguous writes).
 // fp8 cache (OCP E4M3FN, one float32 scale per (request, head, K|V)):
-//   pass 1  every workgroup takes 64 tokens of one request and writes the max |x| per
-//           (K|V, head) of its tokens to the workspace (no atomics across workgroups:
-//           max is exact, so the result does not depend on any order);
-//   pass 2  every workgroup reduces its request's partials, derives scale = a/448 and
-//           inv = 448/a (correctly rounded float32 divisions; a == 0 gives 1 and 1), the
-//           first workgroup of the request stores the scales, and all quantise their
-//           tokens: code = nearest E4M3FN value to x*inv (float32 product), ties to the
-//           even code, saturating at 448.
+//   pass 1  every workgroup takes 64 tokens of one (request, head) and writes the max |x|
+//           of K and of V over them to the workspace (no atomics: max is exact, so the
+//           result does not depend on any order);
+//   pass 2  every workgroup reduces its (request, head)'s partials, derives scale = a/448
+//           and inv = 448/a (correctly rounded float32 divisions; a == 0 gives 1 and 1),
+//           the first workgroup stores the scales, and all quantise their tokens: code =
+//           nearest E4M3FN value to x*inv (float32 product), ties to the even code,
+//           saturating at 448.
+// Every kernel runs one workgroup per (64-token chunk, request, head).
 #include <hip/hip_runtime.h>
 
 #include "qi_internal.h"
@@ -55,93 +56,106 @@ __device__ __forceinline__ uint32_t e4m3fn_from_f32(float y) {
   return sign | code;
 }
 
+// Workgroup (chunk x, request y, head z): tokens [64 x, 64 x + 64) of one request and one
+// head.  Item i of the workgroup is 16-byte chunk i % (D/8) of token i / (D/8): the writes
+// are one contiguous run of the head-major destination.
 __global__ __launch_bounds__(NT) void cache_copy_bf16(const qi_req_dev *__restrict__ reqs,
                                                       int H, int D,
                                                       const uint4 *__restrict__ k_pre,
                                                       const uint4 *__restrict__ v_pre,
                                                       uint8_t *__restrict__ cache) {
   const qi_req_dev r = reqs[blockIdx.y];
-  const int t0 = blockIdx.x * CHUNK;
+  const int t0 = blockIdx.x * CHUNK, h = blockIdx.z;
   if (t0 >= r.lp) return;
   const int nt = min(CHUNK, r.lp - t0);
-  const int cpt = H * D / 8;   // 16-byte chunks per token
-  for (int i = threadIdx.x; i < nt * cpt; i += NT) {
-    const int tok = t0 + i / cpt, rem = i % cpt;
-    const int h = rem / (D / 8), c = rem % (D / 8);
-    const int64_t src = (int64_t)(r.pre_tok + tok) * cpt + rem;
+  const int ch = D / 8;   // 16-byte chunks per (token, head)
+  for (int i = threadIdx.x; i < nt * ch; i += NT) {
+    const int tok = t0 + i / ch, c = i % ch;
+    const int64_t src = ((int64_t)(r.pre_tok + tok) * H + h) * ch + c;
     const int64_t dst = ((int64_t)h * r.lp + tok) * D * 2 + c * 16;
     *reinterpret_cast<uint4 *>(cache + r.k_off + dst) = k_pre[src];
     *reinterpret_cast<uint4 *>(cache + r.v_off + dst) = v_pre[src];
   }
 }
 
+// max over the workgroup of a non-negative float (every thread passes its value)
+__device__ __forceinline__ float block_max(float m, float *red) {
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = red[0];
+  for (int w = 1; w < NT / 64; ++w) m = fmaxf(m, red[w]);
+  __syncthreads();
+  return m;
+}
+
+// Pass 1, workgroup (chunk x, request y, head z): max |x| of K and of V over the chunk's
+// tokens of head z -> partials[part_idx + (x * 2 + K|V) * H + z].
 __global__ __launch_bounds__(NT) void cache_absmax_fp8(const qi_req_dev *__restrict__ reqs,
                                                        int H, int D,
                                                        const uint4 *__restrict__ k_pre,
                                                        const uint4 *__restrict__ v_pre,
                                                        float *__restrict__ partials) {
-  extern __shared__ unsigned int smax[];   // [2][H], float bits of non-negative maxima
+  __shared__ float red[NT / 64];
   const qi_req_dev r = reqs[blockIdx.y];
-  const int t0 = blockIdx.x * CHUNK;
+  const int t0 = blockIdx.x * CHUNK, h = blockIdx.z;
   if (t0 >= r.lp) return;
-  for (int i = threadIdx.x; i < 2 * H; i += NT) smax[i] = 0u;
-  __syncthreads();
   const int nt = min(CHUNK, r.lp - t0);
-  const int cpt = H * D / 8;
-  for (int i = threadIdx.x; i < nt * cpt; i += NT) {
-    const int tok = t0 + i / cpt, rem = i % cpt;
-    const int h = rem / (D / 8);
-    const int64_t src = (int64_t)(r.pre_tok + tok) * cpt + rem;
+  const int ch = D / 8;
+  float m[2] = {0.0f, 0.0f};
+  for (int i = threadIdx.x; i < nt * ch; i += NT) {
+    const int tok = t0 + i / ch, c = i % ch;
+    const int64_t src = ((int64_t)(r.pre_tok + tok) * H + h) * ch + c;
     const uint4 kv[2] = {k_pre[src], v_pre[src]};
 #pragma unroll
     for (int w = 0; w < 2; ++w) {
       const uint32_t x[4] = {kv[w].x, kv[w].y, kv[w].z, kv[w].w};
-      float m = 0.0f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) m = fmaxf(m, fmaxf(fabsf(bf16_lo(x[j])), fabsf(bf16_hi(x[j]))));
-      atomicMax(&smax[w * H + h], __float_as_uint(m));   // LDS atomic; order-free
+      for (int j = 0; j < 4; ++j) m[w] = fmaxf(m[w], fmaxf(fabsf(bf16_lo(x[j])), fabsf(bf16_hi(x[j]))));
     }
   }
-  __syncthreads();
-  for (int i = threadIdx.x; i < 2 * H; i += NT)
-    partials[r.part_idx + blockIdx.x * 2 * H + i] = __uint_as_float(smax[i]);
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    const float a = block_max(m[w], red);
+    if (threadIdx.x == 0) partials[r.part_idx + (blockIdx.x * 2 + w) * H + h] = a;
+  }
 }
 
+// Pass 2, workgroup (chunk x, request y, head z): reduce the request's partials of head z
+// to the scales, store them (chunk 0), quantise the chunk's tokens of head z.
 __global__ __launch_bounds__(NT) void cache_quant_fp8(const qi_req_dev *__restrict__ reqs,
                                                       int H, int D,
                                                       const uint4 *__restrict__ k_pre,
                                                       const uint4 *__restrict__ v_pre,
                                                       const float *__restrict__ partials,
                                                       uint8_t *__restrict__ cache) {
-  extern __shared__ float sinv[];   // [2][H] reciprocal scales
   const qi_req_dev r = reqs[blockIdx.y];
-  const int t0 = blockIdx.x * CHUNK;
+  const int t0 = blockIdx.x * CHUNK, h = blockIdx.z;
   if (t0 >= r.lp) return;
-  for (int i = threadIdx.x; i < 2 * H; i += NT) {
+  float inv[2];
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
     float a = 0.0f;
-    for (int c = 0; c < r.n_chunks; ++c) a = fmaxf(a, partials[r.part_idx + c * 2 * H + i]);
-    const float scale = a > 0.0f ? __fdiv_rn(a, 448.0f) : 1.0f;
-    sinv[i] = a > 0.0f ? __fdiv_rn(448.0f, a) : 1.0f;
-    if (blockIdx.x == 0) reinterpret_cast<float *>(cache + r.s_off)[i] = scale;
+    for (int c = 0; c < r.n_chunks; ++c) a = fmaxf(a, partials[r.part_idx + (c * 2 + w) * H + h]);
+    inv[w] = a > 0.0f ? __fdiv_rn(448.0f, a) : 1.0f;
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+      reinterpret_cast<float *>(cache + r.s_off)[w * H + h] = a > 0.0f ? __fdiv_rn(a, 448.0f) : 1.0f;
   }
-  __syncthreads();
   const int nt = min(CHUNK, r.lp - t0);
-  const int cpt = H * D / 8;
-  for (int i = threadIdx.x; i < nt * cpt; i += NT) {
-    const int tok = t0 + i / cpt, rem = i % cpt;
-    const int h = rem / (D / 8), c = rem % (D / 8);
-    const int64_t src = (int64_t)(r.pre_tok + tok) * cpt + rem;
+  const int ch = D / 8;
+  for (int i = threadIdx.x; i < nt * ch; i += NT) {
+    const int tok = t0 + i / ch, c = i % ch;
+    const int64_t src = ((int64_t)(r.pre_tok + tok) * H + h) * ch + c;
     const int64_t dst = ((int64_t)h * r.lp + tok) * D + c * 8;
     const uint4 kv[2] = {k_pre[src], v_pre[src]};
 #pragma unroll
     for (int w = 0; w < 2; ++w) {
-      const float inv = sinv[w * H + h];
       const uint32_t x[4] = {kv[w].x, kv[w].y, kv[w].z, kv[w].w};
       uint32_t out[2] = {0u, 0u};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t lo = e4m3fn_from_f32(bf16_lo(x[j]) * inv);
-        const uint32_t hi = e4m3fn_from_f32(bf16_hi(x[j]) * inv);
+        const uint32_t lo = e4m3fn_from_f32(bf16_lo(x[j]) * inv[w]);
+        const uint32_t hi = e4m3fn_from_f32(bf16_hi(x[j]) * inv[w]);
         out[j >> 1] |= (lo | (hi << 8)) << (16 * (j & 1));
       }
       *reinterpret_cast<uint2 *>(cache + (w == 0 ? r.k_off : r.v_off) + dst) =
@@ -158,7 +172,7 @@ qi_status qi_launch_cache_write(const qi_plan *p, const void *k_pre, const void 
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t *ws = static_cast<uint8_t *>(p->d_ws);
   const qi_req_dev *reqs = reinterpret_cast<const qi_req_dev *>(ws + p->reqs_off);
-  const dim3 grid(p->max_chunks, p->n_req);
+  const dim3 grid(p->max_chunks, p->n_req, p->H);
   const uint4 *k = static_cast<const uint4 *>(k_pre);
   const uint4 *v = static_cast<const uint4 *>(v_pre);
   uint8_t *c = static_cast<uint8_t *>(cache);
@@ -166,10 +180,9 @@ qi_status qi_launch_cache_write(const qi_plan *p, const void *k_pre, const void 
     hipLaunchKernelGGL(cache_copy_bf16, grid, dim3(NT), 0, s, reqs, p->H, p->D, k, v, c);
   } else {
     float *part = reinterpret_cast<float *>(ws + p->part_off);
-    const size_t sh = 2 * p->H * sizeof(float);
-    hipLaunchKernelGGL(cache_absmax_fp8, grid, dim3(NT), sh, s, reqs, p->H, p->D, k, v, part);
+    hipLaunchKernelGGL(cache_absmax_fp8, grid, dim3(NT), 0, s, reqs, p->H, p->D, k, v, part);
     if (hipGetLastError() != hipSuccess) return QI_ERR_HIP;
-    hipLaunchKernelGGL(cache_quant_fp8, grid, dim3(NT), sh, s, reqs, p->H, p->D, k, v,
+    hipLaunchKernelGGL(cache_quant_fp8, grid, dim3(NT), 0, s, reqs, p->H, p->D, k, v,
                        (const float *)part, c);
   }
   return hipGetLastError() == hipSuccess ? QI_OK : QI_ERR_HIP;
