@@ -108,7 +108,25 @@ def timed(fn, steps, warmup):
     return s.elapsed_time(e)   # ms
 
 
-def measure(name, steps, warmup, layers, dev, with_full=False, with_build=True):
+def capture(fn):
+    """fn captured into a HIP graph on a side stream (torch's capture recipe: one warm-up
+    run on the side stream first)."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def measure(name, steps, warmup, layers, dev, with_full=False, with_build=True,
+            with_graph=False):
     from block_causal_attention_qi_amd import qi
     L = Layers(name, layers, dev, need_full=with_full)
     flops = qi.useful_flops(L.plan, qi.QI_CALL_DENOISE)
@@ -121,6 +139,15 @@ def measure(name, steps, warmup, layers, dev, with_full=False, with_build=True):
     res.update(ms_per_step=ms / steps, ms_per_layer_step=per_launch,
                tflops=flops / (per_launch * 1e-3) / 1e12)
     res["frac_of_peak"] = res["tflops"] / PEAK_BF16_TFLOPS
+    if with_graph:
+        # the whole step (one launch per layer) replayed from a HIP graph: the share of
+        # the eager step that is launch overhead
+        g = capture(L.denoise)
+        gms = timed(g.replay, steps, warmup)
+        res.update(graph_ms_per_step=gms / steps,
+                   graph_tflops=flops * layers / (gms / steps * 1e-3) / 1e12,
+                   launch_overhead_share=max(0.0, 1.0 - gms / ms))
+        del g
     if with_build:
         bflops = qi.useful_flops(L.plan, qi.QI_CALL_PREFIX)
         bms = timed(L.build, max(1, steps // 2), 1) / (max(1, steps // 2) * layers)
@@ -215,7 +242,8 @@ def main():
     dev = torch.device("cuda:0")
     from block_causal_attention_qi_amd import qi  # noqa: F401  (fails loudly if not built)
 
-    main_res = measure(a.workload, a.steps, a.warmup, a.layers, dev, with_full=False)
+    main_res = measure(a.workload, a.steps, a.warmup, a.layers, dev, with_full=False,
+                       with_graph=True)
     log("[bench] %s" % json.dumps(main_res))
     extra = {}
     if not a.no_extra:
@@ -256,11 +284,16 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "kernel": "attn_fwd_kernel<128, bf16 cache>",
+                     "kernel": "attn_pp_kernel<128, bf16 cache>",
                      "flop_per_launch": flops_launch,
                      "ms_per_launch": round(main_res["ms_per_layer_step"], 5)},
         "extra": extra,
     }
+    out["extra"]["graph_replay"] = {
+        "workload": a.workload, "ms_per_step": round(main_res["graph_ms_per_step"], 4),
+        "tflops": round(main_res["graph_tflops"], 3),
+        "launch_overhead_share": round(main_res["launch_overhead_share"], 4),
+        "note": "the same %d-layer step captured once in a HIP graph and replayed" % a.layers}
     if not a.no_cpu:
         out["cpu_baseline"] = cpu_baseline(a.workload)
         log("[bench] cpu baseline %s" % json.dumps(out["cpu_baseline"]))
