@@ -91,6 +91,16 @@ def quantize_prefix(k_pre, v_pre):
     return codes[0], codes[1], scales
 
 
+def quantize_prefix_v(v_pre):
+    """The "fp8_v" cache: V only, [L_p, H, D] -> codes [H, L_p, D] uint8, scales [H]."""
+    lp, nh, d = v_pre.shape
+    codes = np.empty((nh, lp, d), dtype=np.uint8)
+    scales = np.empty(nh, dtype=np.float32)
+    for h in range(nh):
+        codes[h], scales[h] = quantize_slab(np.asarray(v_pre)[:, h, :])
+    return codes, scales
+
+
 def dequantize(codes_hld, scales_h):
     """codes [H, L_p, D] and scales [H] -> values [L_p, H, D] float64 (token-major)."""
     vals = e4m3fn_value(codes_hld) * np.asarray(scales_h, dtype=np.float64)[:, None, None]

@@ -8,9 +8,10 @@ Cache layout (one arena per layer and wave; [recipe] "Prefix KV cache" says the 
 rebuilt for every generation, so it holds exactly the requests of one wave):
   requests follow one another in wave order; each request's region starts on a 256-byte
   boundary and holds, each part again starting on a 256-byte boundary,
-      K  [H][L_p][D]   bf16 (2 bytes) or E4M3FN code (1 byte)
-      V  [H][L_p][D]   same element type
-      scales [2][H]    float32, row 0 for K and row 1 for V  (fp8 caches only)
+      K  [H][L_p][D]   bf16 (2 bytes), or E4M3FN code (1 byte) for the "fp8" cache
+      V  [H][L_p][D]   bf16, or E4M3FN code for the "fp8" and "fp8_v" caches
+      scales [2][H]    float32, row 0 for K and row 1 for V  (fp8 caches only; the
+                       "fp8_v" cache keeps K in bf16 and stores 1.0 as its K scales)
   the arena size is the end of the last region rounded up to 256 bytes.
 
 Tiling (what the attention kernels launch over):
@@ -32,7 +33,18 @@ from .attention import allowed_mask, block_offsets
 ALIGN = 256
 EMPTY, PARTIAL, FULL = 0, 1, 2
 CALL_PREFIX, CALL_DENOISE, CALL_FULL = 0, 1, 2
-KV_BF16, KV_FP8 = 0, 1
+KV_BF16, KV_FP8, KV_FP8_V = 0, 1, 2
+
+
+def _elem_bytes(kv_dtype, which):
+    """Bytes per cached element of K (which = 0) or V (which = 1)."""
+    if kv_dtype == KV_BF16:
+        return 2
+    if kv_dtype == KV_FP8:
+        return 1
+    if kv_dtype == KV_FP8_V:
+        return 2 if which == 0 else 1
+    raise ValueError("unknown cache type")
 
 
 def _align(x):
@@ -41,16 +53,16 @@ def _align(x):
 
 def cache_layout(requests, n_heads, head_dim, kv_dtype):
     """requests: list of block-length lists.  Returns (regions, total_bytes)."""
-    eb = 2 if kv_dtype == KV_BF16 else 1
+    ek, ev = _elem_bytes(kv_dtype, 0), _elem_bytes(kv_dtype, 1)
     regions, off = [], 0
     for bl in requests:
         lp = int(np.sum(bl[:-1]))
         start = _align(off)
         k_off = start
-        v_off = _align(k_off + n_heads * lp * head_dim * eb)
-        end = v_off + n_heads * lp * head_dim * eb
+        v_off = _align(k_off + n_heads * lp * head_dim * ek)
+        end = v_off + n_heads * lp * head_dim * ev
         s_off = None
-        if kv_dtype == KV_FP8:
+        if kv_dtype != KV_BF16:
             s_off = _align(end)
             end = s_off + 2 * n_heads * 4
         regions.append(dict(lp=lp, k_off=k_off, v_off=v_off, s_off=s_off, end=end))
@@ -60,7 +72,7 @@ def cache_layout(requests, n_heads, head_dim, kv_dtype):
 
 def cache_offset(regions, head_dim, kv_dtype, req, kv, head, tok):
     """Byte offset of element (req, K|V, head, token, channel 0) in the arena."""
-    eb = 2 if kv_dtype == KV_BF16 else 1
+    eb = _elem_bytes(kv_dtype, kv)
     reg = regions[req]
     base = reg["k_off"] if kv == 0 else reg["v_off"]
     return base + (head * reg["lp"] + tok) * head_dim * eb
@@ -96,10 +108,15 @@ def cache_image(requests, n_heads, head_dim, kv_dtype, k_pre, v_pre):
         if kv_dtype == KV_BF16:
             parts = [(reg["k_off"], bf16_bits(np.transpose(kr, (1, 0, 2))).view(np.uint8)),
                      (reg["v_off"], bf16_bits(np.transpose(vr, (1, 0, 2))).view(np.uint8))]
-        else:
+        elif kv_dtype == KV_FP8:
             ck, cv, sc = F.quantize_prefix(kr, vr)
             parts = [(reg["k_off"], ck), (reg["v_off"], cv),
                      (reg["s_off"], sc.astype("<f4").view(np.uint8))]
+        else:
+            cv, sv = F.quantize_prefix_v(vr)
+            sc = np.stack([np.ones_like(sv), sv])
+            parts = [(reg["k_off"], bf16_bits(np.transpose(kr, (1, 0, 2))).view(np.uint8)),
+                     (reg["v_off"], cv), (reg["s_off"], sc.astype("<f4").view(np.uint8))]
         for off, arr in parts:
             flat = np.ascontiguousarray(arr).reshape(-1).view(np.uint8)
             img[off:off + flat.size] = flat

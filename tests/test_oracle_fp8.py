@@ -105,3 +105,12 @@ def test_quantize_prefix_shapes_and_roundtrip():
 def test_encoder_rejects_nan():
     with pytest.raises(ValueError):
         fp8.e4m3fn_encode(np.array([np.nan], np.float32))
+
+
+def test_v_only_quantisation_is_the_v_half():
+    rng = np.random.default_rng(8)
+    k = rng.standard_normal((37, 3, 16)) * 3
+    v = rng.standard_normal((37, 3, 16)) * 0.01
+    ck, cv, sc = fp8.quantize_prefix(k, v)
+    cv2, sv = fp8.quantize_prefix_v(v)
+    assert np.array_equal(cv, cv2) and np.array_equal(sc[1], sv)

@@ -107,6 +107,13 @@ def test_cache_layout_worked_example():
     assert (regs[0]["v_off"], regs[0]["s_off"], regs[0]["end"], total) == (256, 512, 520, 768)
     regs, total = L.cache_layout([[3, 4]], 1, 64, L.KV_BF16)
     assert (regs[0]["v_off"], regs[0]["end"], total) == (512, 896, 1024)
+    # V-only fp8: K bf16 (2 B), V codes (1 B), scales [2][H]
+    regs, total = L.cache_layout([[3, 5, 4], [2, 6]], 2, 64, L.KV_FP8_V)
+    assert [(r["k_off"], r["v_off"], r["s_off"], r["end"]) for r in regs] == \
+        [(0, 2048, 3072, 3088), (3328, 3840, 4096, 4112)]
+    assert total == 4352
+    assert L.cache_offset(regs, 64, L.KV_FP8_V, 1, 0, 1, 1) == 3328 + (2 + 1) * 64 * 2
+    assert L.cache_offset(regs, 64, L.KV_FP8_V, 1, 1, 1, 1) == 3840 + (2 + 1) * 64
 
 
 # ---------------------------------------------------------------- page facts
@@ -150,7 +157,7 @@ def test_cache_image_reads_back_through_offsets():
     kf = torch.from_numpy(rng.standard_normal((lp, h, d)).astype(np.float32)).to(torch.bfloat16)
     vf = torch.from_numpy(rng.standard_normal((lp, h, d)).astype(np.float32) * 2).to(torch.bfloat16)
     k64, v64 = kf.double().numpy(), vf.double().numpy()
-    for kv_dtype in (L.KV_BF16, L.KV_FP8):
+    for kv_dtype in (L.KV_BF16, L.KV_FP8, L.KV_FP8_V):
         img, defined = L.cache_image(reqs, h, d, kv_dtype, k64, v64)
         regs, total = L.cache_layout(reqs, h, d, kv_dtype)
         assert img.size == total
@@ -159,13 +166,16 @@ def test_cache_image_reads_back_through_offsets():
             n = sum(bl[:-1])
             for which, src in ((0, kf), (1, vf)):
                 x = src[tok0:tok0 + n]                       # [n, h, d]
-                if kv_dtype == L.KV_FP8:
+                if kv_dtype != L.KV_BF16:
                     s_off = regs[r]["s_off"]
                     scales = img[s_off:s_off + 8 * h].view("<f4").reshape(2, h)
+                coded = kv_dtype == L.KV_FP8 or (kv_dtype == L.KV_FP8_V and which == 1)
+                if kv_dtype == L.KV_FP8_V and which == 0:
+                    assert np.all(scales[0] == 1.0)
                 for hh in range(h):
                     for t in range(n):
                         off = L.cache_offset(regs, d, kv_dtype, r, which, hh, t)
-                        if kv_dtype == L.KV_BF16:
+                        if not coded:
                             want = x[t, hh].view(torch.int16).numpy().view(np.uint8)
                             got = img[off:off + 2 * d]
                         else:
@@ -178,6 +188,6 @@ def test_cache_image_reads_back_through_offsets():
                         assert defined[off:off + got.size].all()
             tok0 += n
         # everything defined is accounted for by K, V (and scales)
-        eb = 2 if kv_dtype == L.KV_BF16 else 1
-        extra = 8 * h * len(reqs) if kv_dtype == L.KV_FP8 else 0
-        assert defined.sum() == 2 * lp * h * d * eb + extra
+        eb = {L.KV_BF16: 4, L.KV_FP8: 2, L.KV_FP8_V: 3}[kv_dtype]   # K + V bytes per element
+        extra = 8 * h * len(reqs) if kv_dtype != L.KV_BF16 else 0
+        assert defined.sum() == lp * h * d * eb + extra
