@@ -43,10 +43,13 @@ class Layers:
     """Per-layer device buffers of one workload: layer l holds the base inputs rolled by
     97*l tokens (same distribution, different bytes)."""
 
-    def __init__(self, name, layers, dev, need_full=False):
+    def __init__(self, name, layers, dev, need_full=False, kv=None):
+        import dataclasses
         import torch
         from block_causal_attention_qi_amd import qi, synth
         self.w = synth.WORKLOADS[name]
+        if kv is not None:
+            self.w = dataclasses.replace(self.w, kv_dtype=kv)
         w = self.w
         t0 = time.time()
         x = synth.generate(w, steps=1)
@@ -126,9 +129,9 @@ def capture(fn):
 
 
 def measure(name, steps, warmup, layers, dev, with_full=False, with_build=True,
-            with_graph=False):
+            with_graph=False, kv=None):
     from block_causal_attention_qi_amd import qi
-    L = Layers(name, layers, dev, need_full=with_full)
+    L = Layers(name, layers, dev, need_full=with_full, kv=kv)
     flops = qi.useful_flops(L.plan, qi.QI_CALL_DENOISE)
     res = {"workload": name, "requests": L.w.requests, "heads": L.w.n_heads,
            "head_dim": L.w.head_dim, "kv_cache": L.w.kv_dtype, "layers": layers,
@@ -157,12 +160,13 @@ def measure(name, steps, warmup, layers, dev, with_full=False, with_build=True,
         fms = timed(L.full, max(1, steps // 2), 1) / (max(1, steps // 2) * layers)
         res.update(full_ms_per_layer=fms, full_tflops=fflops / (fms * 1e-3) / 1e12,
                    cached_speedup_vs_full=fms / per_launch)
-    if L.w.kv_dtype == "fp8":
+    if L.w.kv_dtype != "bf16":
         # compulsory bytes of one denoising launch: image Q/K/V read + O written (bf16)
-        # plus the fp8 prefix cache read once
+        # plus the prefix cache read once (fp8: 1 byte for K and V; fp8_v: 2 for K, 1 for V)
         pre, img, _ = qi.qi_plan_tokens(L.plan)
         hd = L.w.n_heads * L.w.head_dim
-        byts = 4 * img * hd * 2 + 2 * pre * hd + 8 * L.w.n_heads * len(L.w.requests)
+        per_tok = 2 if L.w.kv_dtype == "fp8" else 3
+        byts = 4 * img * hd * 2 + per_tok * pre * hd + 8 * L.w.n_heads * len(L.w.requests)
         res["compulsory_gb_per_s"] = byts / (per_launch * 1e-3) / 1e9
     del L
     import torch
@@ -221,7 +225,8 @@ def main():
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--workload", default="t2i1024")
     ap.add_argument("--extra", action="store_true",
-                    help="also time edit2048, edit4 (cached vs full) and wave8 (fp8)")
+                    help="also time edit4 (cached vs full), wave8 (fp8) and edit10 (ten "
+                         "references: cached vs full, and the fp8 / fp8_v caches)")
     ap.add_argument("--no-extra", action="store_true", help="time only the main workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -253,6 +258,13 @@ def main():
                 continue
             extra[n] = measure(n, max(2, a.steps // 2), 1, a.layers, dev, with_full=(n == "edit4"))
             log("[bench] %s" % json.dumps(extra[n]))
+        if a.extra:
+            # ten references: ~2.4 GB of buffers per layer, so 8 layers
+            for kv in ("bf16", "fp8", "fp8_v"):
+                key = "edit10" if kv == "bf16" else "edit10_" + kv
+                extra[key] = measure("edit10", 2, 1, min(a.layers, 8), dev,
+                                     with_full=(kv == "bf16"), with_build=(kv == "bf16"), kv=kv)
+                log("[bench] %s" % json.dumps(extra[key]))
 
     traffic = None
     try:

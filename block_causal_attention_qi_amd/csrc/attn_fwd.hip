@@ -65,7 +65,12 @@ constexpr int NT = 512;                 // ping-pong kernel: 8 wavefronts
 constexpr int NT_STAGED = 256;          // register-staged kernel: 4 wavefronts
 constexpr float TAU = 8.0f;   // lazy-rescale threshold, log2 units
 
-enum { SRC_ONE = 0, SRC_CACHE_BF16 = 1, SRC_CACHE_FP8 = 2 };
+enum { SRC_ONE = 0, SRC_CACHE_BF16 = 1, SRC_CACHE_FP8 = 2, SRC_CACHE_FP8V = 3 };
+
+// Whether cached K (which = 0) or V (which = 1) rows are E4M3FN codes for a source kind.
+__host__ __device__ constexpr bool coded(int src, int which) {
+  return src == SRC_CACHE_FP8 || (src == SRC_CACHE_FP8V && which == 1);
+}
 
 template <int D>
 struct Cfg {
@@ -256,8 +261,9 @@ struct Direct {
 };
 
 // ---------------------------------------------------------------------------------------
-// Register-staged tile loads (fp8 cache): lane t stages chunk t % CH of rows
-// t / CH + i * ROWS (i < PASS) of both tiles and dequantises cached rows on the way.
+// Register-staged tile loads (fp8 caches): lane t stages chunk t % CH of rows
+// t / CH + i * ROWS (i < PASS) of both tiles and dequantises cached rows on the way (K
+// and V of the fp8 cache, V only of the V-only cache).
 template <int D, int SRC>
 struct Stage {
   using C = Cfg<D>;
@@ -278,14 +284,22 @@ struct Stage {
     }
   }
 
+  // 8 elements of a cached row: 8 codes in the low half, or 8 bf16
+  template <bool CODED>
+  __device__ __forceinline__ static uint4 cached8(const uint8_t *row_base, int64_t off) {
+    if (CODED) {
+      const uint2 raw = *reinterpret_cast<const uint2 *>(row_base + off);
+      return make_uint4(raw.x, raw.y, 0, 0);
+    }
+    return *reinterpret_cast<const uint4 *>(row_base + 2 * off);
+  }
+
+  template <bool CODED>
   __device__ __forceinline__ uint4 fetch_row(const __bf16 *live, int64_t coff, int key,
                                              const TileArgs &a) const {
     if (key >= a.kend) return make_uint4(0, 0, 0, 0);
-    if (SRC != SRC_ONE && key < a.lp) {
-      const uint8_t *p = a.cache + coff + (int64_t)(a.h * a.lp + key) * D + chunk * 8;
-      const uint2 raw = *reinterpret_cast<const uint2 *>(p);
-      return make_uint4(raw.x, raw.y, 0, 0);
-    }
+    if (SRC != SRC_ONE && key < a.lp)
+      return cached8<CODED>(a.cache + coff, (int64_t)(a.h * a.lp + key) * D + chunk * 8);
     const __bf16 *p = live + ((int64_t)(a.kv_tok + key - a.lp) * a.H + a.h) * D + chunk * 8;
     return *reinterpret_cast<const uint4 *>(p);
   }
@@ -303,20 +317,19 @@ struct Stage {
       }
     } else if (kd == CACHED) {
       const int64_t e0 = (int64_t)(a.h * a.lp + k0) * D;
-      const uint8_t *kb = a.cache + a.k_off + e0, *vb = a.cache + a.v_off + e0;
+      const uint8_t *kb = a.cache + a.k_off + e0 * (coded(SRC, 0) ? 1 : 2);
+      const uint8_t *vb = a.cache + a.v_off + e0 * (coded(SRC, 1) ? 1 : 2);
 #pragma unroll
       for (int i = 0; i < C::PASS; ++i) {
-        const uint2 x = *reinterpret_cast<const uint2 *>(kb + cache_off[i]);
-        const uint2 y = *reinterpret_cast<const uint2 *>(vb + cache_off[i]);
-        kr[i] = make_uint4(x.x, x.y, 0, 0);
-        vr[i] = make_uint4(y.x, y.y, 0, 0);
+        kr[i] = cached8<coded(SRC, 0)>(kb, cache_off[i]);
+        vr[i] = cached8<coded(SRC, 1)>(vb, cache_off[i]);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < C::PASS; ++i) {
         const int key = k0 + row0 + i * C::ROWS;
-        kr[i] = fetch_row(a.k, a.k_off, key, a);
-        vr[i] = fetch_row(a.v, a.v_off, key, a);
+        kr[i] = fetch_row<coded(SRC, 0)>(a.k, a.k_off, key, a);
+        vr[i] = fetch_row<coded(SRC, 1)>(a.v, a.v_off, key, a);
       }
     }
   }
@@ -328,8 +341,8 @@ struct Stage {
       const int r = row0 + i * C::ROWS;
       uint4 kv = kr[i], vv = vr[i];
       if (kd == CACHED || (kd == MIXED && kt * BN + r < a.lp && kt * BN + r < a.kend)) {
-        kv = dequant8(kv.x, kv.y, a.k_scale);
-        vv = dequant8(vv.x, vv.y, a.v_scale);
+        if (coded(SRC, 0)) kv = dequant8(kv.x, kv.y, a.k_scale);
+        if (coded(SRC, 1)) vv = dequant8(vv.x, vv.y, a.v_scale);
       }
       *reinterpret_cast<uint4 *>(reinterpret_cast<char *>(Ks) + C::koff(r, chunk)) = kv;
       *reinterpret_cast<uint4 *>(reinterpret_cast<char *>(Vs) + C::voff(r, chunk)) = vv;
@@ -766,7 +779,7 @@ __global__ __launch_bounds__(NT_STAGED, 2) void attn_staged_kernel(
   if (item < 0) return;
   const qi_tile tl = tiles[item / H];
   const int h = item % H;
-  const TileArgs a = make_args(tl, H, h, k, v, cache, SRC == SRC_CACHE_FP8);
+  const TileArgs a = make_args(tl, H, h, k, v, cache, SRC == SRC_CACHE_FP8 || SRC == SRC_CACHE_FP8V);
   const int row = (threadIdx.x >> 6) * 32 + (threadIdx.x & 31);
   const bool active = (threadIdx.x >> 6) * 32 < tl.nrows;
 
@@ -808,8 +821,13 @@ qi_status launch(const qi_plan *p, int call, const void *q, const void *k, const
                  void *o, const void *cache, hipStream_t s) {
   const uint8_t *ws = static_cast<const uint8_t *>(p->d_ws);
   const float c = (float)(1.4426950408889634 / std::sqrt((double)D));   // log2(e)/sqrt(D)
-  auto kern = SRC == SRC_CACHE_FP8 ? attn_staged_kernel<D, SRC> : attn_pp_kernel<D, SRC>;
-  const int nt = SRC == SRC_CACHE_FP8 ? NT_STAGED : NT;
+  constexpr bool staged = SRC == SRC_CACHE_FP8 || SRC == SRC_CACHE_FP8V;
+  decltype(&attn_pp_kernel<D, SRC_ONE>) kern;
+  if constexpr (staged)
+    kern = attn_staged_kernel<D, SRC>;
+  else
+    kern = attn_pp_kernel<D, SRC>;
+  const int nt = staged ? NT_STAGED : NT;
   hipLaunchKernelGGL(kern, dim3(p->sched_len[call]), dim3(nt), 0, s,
                      reinterpret_cast<const int32_t *>(ws + p->sched_off[call]),
                      reinterpret_cast<const qi_tile *>(ws + p->tiles_off[call]), p->H,
@@ -826,13 +844,16 @@ qi_status qi_launch_attention(const qi_plan *p, int call, const void *q, const v
   if (p->sched_len[call] == 0) return QI_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int src = call != QI_CALL_DENOISE ? SRC_ONE
-                                          : (p->kv == QI_KV_BF16 ? SRC_CACHE_BF16 : SRC_CACHE_FP8);
+                  : p->kv == QI_KV_BF16 ? SRC_CACHE_BF16
+                  : p->kv == QI_KV_FP8_E4M3 ? SRC_CACHE_FP8 : SRC_CACHE_FP8V;
   if (p->D == 128) {
     if (src == SRC_ONE) return launch<128, SRC_ONE>(p, call, q, k, v, o, cache, s);
     if (src == SRC_CACHE_BF16) return launch<128, SRC_CACHE_BF16>(p, call, q, k, v, o, cache, s);
-    return launch<128, SRC_CACHE_FP8>(p, call, q, k, v, o, cache, s);
+    if (src == SRC_CACHE_FP8) return launch<128, SRC_CACHE_FP8>(p, call, q, k, v, o, cache, s);
+    return launch<128, SRC_CACHE_FP8V>(p, call, q, k, v, o, cache, s);
   }
   if (src == SRC_ONE) return launch<64, SRC_ONE>(p, call, q, k, v, o, cache, s);
   if (src == SRC_CACHE_BF16) return launch<64, SRC_CACHE_BF16>(p, call, q, k, v, o, cache, s);
-  return launch<64, SRC_CACHE_FP8>(p, call, q, k, v, o, cache, s);
+  if (src == SRC_CACHE_FP8) return launch<64, SRC_CACHE_FP8>(p, call, q, k, v, o, cache, s);
+  return launch<64, SRC_CACHE_FP8V>(p, call, q, k, v, o, cache, s);
 }

@@ -213,7 +213,8 @@ qi_status qi_plan_create(const qi_wave_desc *d, qi_plan **out) {
   if (!d || !d->n_refs || !d->block_len) return QI_ERR_INVALID_ARG;
   if (d->n_requests < 1 || d->n_requests > QI_MAX_REQUESTS) return QI_ERR_INVALID_ARG;
   if (d->n_heads < 1 || d->n_heads > QI_MAX_HEADS) return QI_ERR_INVALID_ARG;
-  if (d->kv_dtype != QI_KV_BF16 && d->kv_dtype != QI_KV_FP8_E4M3) return QI_ERR_INVALID_ARG;
+  if (d->kv_dtype != QI_KV_BF16 && d->kv_dtype != QI_KV_FP8_E4M3 && d->kv_dtype != QI_KV_FP8_V)
+    return QI_ERR_INVALID_ARG;
   if (d->head_dim != 64 && d->head_dim != 128) return QI_ERR_UNSUPPORTED;
 
   qi_plan *p = new (std::nothrow) qi_plan();
@@ -222,7 +223,7 @@ qi_status qi_plan_create(const qi_wave_desc *d, qi_plan **out) {
   p->H = d->n_heads;
   p->D = d->head_dim;
   p->kv = d->kv_dtype;
-  const int eb = p->kv == QI_KV_BF16 ? 2 : 1;
+  const int ebk = qi_cache_elem_bytes(p->kv, 0), ebv = qi_cache_elem_bytes(p->kv, 1);
 
   // requests, block offsets, packed token bases, cache layout
   size_t pos = 0, cache_end = 0;
@@ -250,11 +251,11 @@ qi_status qi_plan_create(const qi_wave_desc *d, qi_plan **out) {
     p->tot_pre += rq.lp;
     p->tot_img += rq.nimg;
     p->tot_all += rq.n;
-    const size_t part = (size_t)p->H * rq.lp * p->D * eb;
+    const size_t elems = (size_t)p->H * rq.lp * p->D;
     rq.k_off = (int64_t)align_up(cache_end);
-    rq.v_off = (int64_t)align_up(rq.k_off + part);
-    rq.end = rq.v_off + (int64_t)part;
-    if (p->kv == QI_KV_FP8_E4M3) {
+    rq.v_off = (int64_t)align_up(rq.k_off + elems * ebk);
+    rq.end = rq.v_off + (int64_t)(elems * ebv);
+    if (p->kv != QI_KV_BF16) {
       rq.s_off = (int64_t)align_up(rq.end);
       rq.end = rq.s_off + 2 * 4 * p->H;
     }
@@ -300,7 +301,7 @@ qi_status qi_plan_create(const qi_wave_desc *d, qi_plan **out) {
   // so every row runs the same kernel path over the same key tiles in every call and the
   // results agree bit for bit (reuse is exact).
   for (int c : {QI_CALL_PREFIX, QI_CALL_DENOISE}) {
-    p->bm[c] = (c == QI_CALL_DENOISE && p->kv == QI_KV_FP8_E4M3) ? QI_ROWS_FP8 : QI_ROWS_BF16;
+    p->bm[c] = (c == QI_CALL_DENOISE && p->kv != QI_KV_BF16) ? QI_ROWS_FP8 : QI_ROWS_BF16;
     build_tiles(*p, c, tiles[c]);
     std::vector<std::pair<int, int>> items;
     for (int t = 0; t < (int)tiles[c].size(); ++t)
@@ -348,7 +349,7 @@ qi_status qi_plan_create(const qi_wave_desc *d, qi_plan **out) {
     off = align_up(off + sched[c].size() * sizeof(int32_t));
   }
   p->part_off = off;
-  p->part_floats = p->kv == QI_KV_FP8_E4M3 ? nparts : 0;
+  p->part_floats = p->kv != QI_KV_BF16 ? nparts : 0;
   off = align_up(off + p->part_floats * sizeof(float));
   p->ws_bytes = off;
   p->ws_image.assign(p->part_off, 0);
@@ -414,12 +415,12 @@ qi_status qi_plan_cache_offset(const qi_plan *p, int32_t req, int32_t kv, int32_
   if (!p || !byte_off || req < 0 || req >= p->n_req || kv < 0 || kv > 2) return QI_ERR_INVALID_ARG;
   const qi_req_host &rq = p->req[req];
   if (kv == 2) {
-    if (p->kv != QI_KV_FP8_E4M3) return QI_ERR_INVALID_ARG;
+    if (p->kv == QI_KV_BF16) return QI_ERR_INVALID_ARG;
     *byte_off = (size_t)rq.s_off;
     return QI_OK;
   }
   if (head < 0 || head >= p->H || tok < 0 || tok >= rq.lp) return QI_ERR_INVALID_ARG;
-  const size_t eb = p->kv == QI_KV_BF16 ? 2 : 1;
+  const size_t eb = qi_cache_elem_bytes(p->kv, kv);
   *byte_off = (size_t)(kv == 0 ? rq.k_off : rq.v_off) + ((size_t)head * rq.lp + tok) * p->D * eb;
   return QI_OK;
 }

@@ -11,7 +11,8 @@
 // contiguous run for the attention kernel's tile loads.
 //
 // bf16 cache: one pass, a re-layout copy (16 bytes per lane, contiguous writes).
-// fp8 cache (OCP E4M3FN, one float32 scale per (request, head, K|V)):
+// fp8 caches (OCP E4M3FN, one float32 scale per (request, head, K|V); the V-only cache
+// keeps K in bf16 with scale 1):
 //   pass 1  every workgroup takes 64 tokens of one (request, head) and writes the max |x|
 //           of K and of V over them to the workspace (no atomics: max is exact, so the
 //           result does not depend on any order);
@@ -122,7 +123,9 @@ __global__ __launch_bounds__(NT) void cache_absmax_fp8(const qi_req_dev *__restr
 }
 
 // Pass 2, workgroup (chunk x, request y, head z): reduce the request's partials of head z
-// to the scales, store them (chunk 0), quantise the chunk's tokens of head z.
+// to the scales, store them (chunk 0), quantise the chunk's tokens of head z.  K8 false
+// (the V-only cache): K is copied as bf16 and its scale stored as 1.
+template <bool K8>
 __global__ __launch_bounds__(NT) void cache_quant_fp8(const qi_req_dev *__restrict__ reqs,
                                                       int H, int D,
                                                       const uint4 *__restrict__ k_pre,
@@ -138,8 +141,9 @@ __global__ __launch_bounds__(NT) void cache_quant_fp8(const qi_req_dev *__restri
     float a = 0.0f;
     for (int c = 0; c < r.n_chunks; ++c) a = fmaxf(a, partials[r.part_idx + (c * 2 + w) * H + h]);
     inv[w] = a > 0.0f ? __fdiv_rn(448.0f, a) : 1.0f;
+    const float scale = (w == 0 && !K8) ? 1.0f : a > 0.0f ? __fdiv_rn(a, 448.0f) : 1.0f;
     if (blockIdx.x == 0 && threadIdx.x == 0)
-      reinterpret_cast<float *>(cache + r.s_off)[w * H + h] = a > 0.0f ? __fdiv_rn(a, 448.0f) : 1.0f;
+      reinterpret_cast<float *>(cache + r.s_off)[w * H + h] = scale;
   }
   const int nt = min(CHUNK, r.lp - t0);
   const int ch = D / 8;
@@ -148,8 +152,9 @@ __global__ __launch_bounds__(NT) void cache_quant_fp8(const qi_req_dev *__restri
     const int64_t src = ((int64_t)(r.pre_tok + tok) * H + h) * ch + c;
     const int64_t dst = ((int64_t)h * r.lp + tok) * D + c * 8;
     const uint4 kv[2] = {k_pre[src], v_pre[src]};
+    if (!K8) *reinterpret_cast<uint4 *>(cache + r.k_off + dst * 2) = kv[0];
 #pragma unroll
-    for (int w = 0; w < 2; ++w) {
+    for (int w = K8 ? 0 : 1; w < 2; ++w) {
       const uint32_t x[4] = {kv[w].x, kv[w].y, kv[w].z, kv[w].w};
       uint32_t out[2] = {0u, 0u};
 #pragma unroll
@@ -182,8 +187,8 @@ qi_status qi_launch_cache_write(const qi_plan *p, const void *k_pre, const void 
     float *part = reinterpret_cast<float *>(ws + p->part_off);
     hipLaunchKernelGGL(cache_absmax_fp8, grid, dim3(NT), 0, s, reqs, p->H, p->D, k, v, part);
     if (hipGetLastError() != hipSuccess) return QI_ERR_HIP;
-    hipLaunchKernelGGL(cache_quant_fp8, grid, dim3(NT), 0, s, reqs, p->H, p->D, k, v,
-                       (const float *)part, c);
+    auto quant = p->kv == QI_KV_FP8_E4M3 ? cache_quant_fp8<true> : cache_quant_fp8<false>;
+    hipLaunchKernelGGL(quant, grid, dim3(NT), 0, s, reqs, p->H, p->D, k, v, (const float *)part, c);
   }
   return hipGetLastError() == hipSuccess ? QI_OK : QI_ERR_HIP;
 }

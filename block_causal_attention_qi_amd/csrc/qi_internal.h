@@ -75,6 +75,11 @@ struct qi_plan {
   bool built = false;     // a prefix build has been enqueued on this plan
 };
 
+// Bytes per cached element of K (which = 0) or V (which = 1) for a cache type.
+inline int qi_cache_elem_bytes(int kv, int which) {
+  return kv == QI_KV_BF16 ? 2 : kv == QI_KV_FP8_E4M3 ? 1 : (which == 0 ? 2 : 1);
+}
+
 // Kernel launchers (defined in the .hip files).  Return QI_OK or QI_ERR_HIP.
 qi_status qi_launch_attention(const qi_plan *p, int call, const void *q, const void *k,
                               const void *v, void *o, const void *cache, void *stream);

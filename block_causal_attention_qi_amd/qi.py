@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libqi.so")
 
 QI_OK, QI_ERR_INVALID_ARG, QI_ERR_UNSUPPORTED, QI_ERR_STATE, QI_ERR_BUFFER_TOO_SMALL, \
     QI_ERR_HIP = range(6)
-QI_KV_BF16, QI_KV_FP8_E4M3 = 0, 1
+QI_KV_BF16, QI_KV_FP8_E4M3, QI_KV_FP8_V = 0, 1, 2
 QI_CALL_PREFIX, QI_CALL_DENOISE, QI_CALL_FULL = 0, 1, 2
 QI_MAX_REQUESTS, QI_MAX_REFS, QI_MAX_HEADS = 64, 10, 128
 
@@ -95,7 +95,7 @@ class Plan:
         self.requests = [list(map(int, b)) for b in requests]
         self.n_heads, self.head_dim = int(n_heads), int(head_dim)
         self.kv_dtype = kv_dtype
-        kv = {"bf16": QI_KV_BF16, "fp8": QI_KV_FP8_E4M3}.get(kv_dtype, kv_dtype)
+        kv = {"bf16": QI_KV_BF16, "fp8": QI_KV_FP8_E4M3, "fp8_v": QI_KV_FP8_V}.get(kv_dtype, kv_dtype)
         n_refs = [len(b) - 2 for b in self.requests]
         flat = [x for b in self.requests for x in b]
         self._refs = (ctypes.c_int32 * max(1, len(n_refs)))(*n_refs)

@@ -39,7 +39,7 @@ class Workload:
     n_heads: int
     head_dim: int
     requests: list                 # list of block-length lists [text, refs..., image]
-    kv_dtype: str = "bf16"         # prefix cache element type: "bf16" or "fp8"
+    kv_dtype: str = "bf16"         # prefix cache element type: "bf16", "fp8" or "fp8_v"
     steps: int = 40                # denoising steps per request
     layers: int = 32               # DiT layers (each has its own cache)
     note: str = ""
@@ -76,6 +76,9 @@ WORKLOADS = {
                          note="2048x2048 edit with one reference, 128x128 latent"),
     "wave8": Workload("wave8", 4, 24, 128, _wave8_requests(), kv_dtype="fp8",
                       note="eight 1024x1024 requests at one phase, fp8 prefix cache"),
+    "edit10": Workload("edit10", 5, 24, 128, [[256] + [4096] * 10 + [4096]],
+                       note="1024x1024 edit with ten references (the model's maximum), "
+                            "41,216 prefix tokens"),
 }
 
 

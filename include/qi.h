@@ -32,13 +32,14 @@
  *     full step    : [sum_r N(r)][H][D]     text, ref_1..ref_R, image of each request
  *   prefix cache (one arena per layer and wave): requests in wave order, each region
  *   256-byte aligned and holding, each part again 256-byte aligned,
- *     K [H][L_p][D], then V [H][L_p][D]      bf16, or OCP E4M3FN codes (1 byte) for fp8
- *     scales [2][H] float32 (row 0 K, row 1 V) fp8 caches only
- *   The fp8 cache is one of the pages' storage options ("fp8": K and V; recipe section
- *   "Prefix KV cache").  Quantisation: per (request, head, K|V) a = max|x| over all prefix
- *   tokens and channels, scale = a/448, inv = 448/a (float32, correctly rounded; a == 0
- *   gives 1 and 1), code = nearest E4M3FN value to the float32 product x*inv, ties to
- *   even, saturating at +-448.  Attention reads code*scale rounded to bf16.
+ *     K [H][L_p][D], then V [H][L_p][D]      bf16, or OCP E4M3FN codes (1 byte): K and V
+ *                                            for QI_KV_FP8_E4M3, V only for QI_KV_FP8_V
+ *     scales [2][H] float32 (row 0 K, row 1 V) fp8 caches only (QI_KV_FP8_V: K row = 1)
+ *   The fp8 caches are the pages' storage options ("fp8": K and V, "fp8_v": V only;
+ *   recipe section "Prefix KV cache").  Quantisation: per (request, head, K|V) a = max|x|
+ *   over all prefix tokens and channels, scale = a/448, inv = 448/a (float32, correctly
+ *   rounded; a == 0 gives 1 and 1), code = nearest E4M3FN value to the float32 product
+ *   x*inv, ties to even, saturating at +-448.  Attention reads code*scale rounded to bf16.
  *
  * Ownership and errors.  The caller owns every device buffer (inputs, outputs, the
  * cache arena, the plan workspace) and the stream; the library owns only the host-side
@@ -70,7 +71,10 @@ typedef enum qi_status {
   QI_ERR_HIP = 5               /* a HIP runtime call or kernel launch failed              */
 } qi_status;
 
-typedef enum qi_kv_dtype { QI_KV_BF16 = 0, QI_KV_FP8_E4M3 = 1 } qi_kv_dtype;
+/* Prefix cache element type: bf16 K and V; fp8 K and V ("fp8"); bf16 K and fp8 V ("fp8_v").
+ * The two fp8 options are the recipe's (vLLM recipe "Qwen/Qwen-Image-2.1", section
+ * "Prefix KV cache"). */
+typedef enum qi_kv_dtype { QI_KV_BF16 = 0, QI_KV_FP8_E4M3 = 1, QI_KV_FP8_V = 2 } qi_kv_dtype;
 
 typedef enum qi_call { QI_CALL_PREFIX = 0, QI_CALL_DENOISE = 1, QI_CALL_FULL = 2 } qi_call;
 

@@ -96,10 +96,16 @@ def split(w, arr, which):
 
 def oracle_prefix_values(w, e, kv):
     """Per request: the prefix K/V the denoising step reads (bf16 values, or the
-    dequantised fp8 cache)."""
+    dequantised fp8 cache: K and V for "fp8", V only for "fp8_v")."""
     ks, vs = split(w, e["k_pre"], "pre"), split(w, e["v_pre"], "pre")
     if kv == "bf16":
         return ks, vs
+    if kv == "fp8_v":
+        out_v = []
+        for v in vs:
+            cv, sv = F.quantize_prefix_v(v)
+            out_v.append(F.dequantize(cv, sv))
+        return ks, out_v
     out_k, out_v = [], []
     for k, v in zip(ks, vs):
         ck, cv, sc = F.quantize_prefix(k, v)

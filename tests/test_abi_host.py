@@ -43,7 +43,7 @@ def test_library_exports_every_declared_call():
 
 @pytest.mark.parametrize("reqs,h,d", WAVES)
 def test_tile_maps_match_oracle(reqs, h, d):
-    for kv in ("bf16", "fp8"):
+    for kv in ("bf16", "fp8", "fp8_v"):
         p = qi.Plan(reqs, h, d, kv)
         for call in (qi.QI_CALL_PREFIX, qi.QI_CALL_DENOISE, qi.QI_CALL_FULL):
             tilings = [qi.qi_plan_kernel_tile(p, call), (64, 64), (128, 128), (256, 64)]
@@ -58,7 +58,7 @@ def test_tile_maps_match_oracle(reqs, h, d):
 @pytest.mark.parametrize("reqs,h,d", WAVES)
 def test_cache_layout_and_pairs_match_oracle(reqs, h, d):
     rng = np.random.default_rng(7)
-    for kv_name, kv in (("bf16", L.KV_BF16), ("fp8", L.KV_FP8)):
+    for kv_name, kv in (("bf16", L.KV_BF16), ("fp8", L.KV_FP8), ("fp8_v", L.KV_FP8_V)):
         p = qi.Plan(reqs, h, d, kv_name)
         regs, total = L.cache_layout(reqs, h, d, kv)
         assert p.cache_bytes == total
@@ -70,7 +70,7 @@ def test_cache_layout_and_pairs_match_oracle(reqs, h, d):
                     for t in toks:
                         assert qi.qi_plan_cache_offset(p, r, which, head, t) == \
                             L.cache_offset(regs, d, kv, r, which, head, t)
-            if kv == L.KV_FP8:
+            if kv != L.KV_BF16:
                 assert qi.qi_plan_cache_offset(p, r, 2, 0, 0) == regs[r]["s_off"]
         for call in (L.CALL_PREFIX, L.CALL_DENOISE, L.CALL_FULL):
             assert qi.qi_plan_pairs(p, call) == sum(L.useful_pairs(b, call) for b in reqs)
@@ -109,7 +109,8 @@ def test_plan_create_argument_checks():
     assert _raw_create(1, [1], [3, 4, 5], 129, 64, 0) == qi.QI_ERR_INVALID_ARG
     assert _raw_create(1, [1], [3, 4, 5], 2, 96, 0) == qi.QI_ERR_UNSUPPORTED
     assert _raw_create(1, [1], [3, 4, 5], 2, 256, 0) == qi.QI_ERR_UNSUPPORTED
-    assert _raw_create(1, [1], [3, 4, 5], 2, 64, 2) == qi.QI_ERR_INVALID_ARG
+    assert _raw_create(1, [1], [3, 4, 5], 2, 64, 2) == qi.QI_OK   # V-only fp8 cache
+    assert _raw_create(1, [1], [3, 4, 5], 2, 64, 3) == qi.QI_ERR_INVALID_ARG
     assert _raw_create(1, [0], [1 << 23, 1 << 23], 1, 64, 0) == qi.QI_ERR_INVALID_ARG
     # null descriptor / output
     assert qi.lib.qi_plan_create(None, ctypes.byref(ctypes.c_void_p())) == qi.QI_ERR_INVALID_ARG

@@ -23,7 +23,7 @@ pytestmark = pytest.mark.gpu
 
 def _cache_matches_oracle(gw, e):
     w = gw.w
-    kvn = L.KV_BF16 if gw.kv == "bf16" else L.KV_FP8
+    kvn = {"bf16": L.KV_BF16, "fp8": L.KV_FP8, "fp8_v": L.KV_FP8_V}[gw.kv]
     img, defined = L.cache_image(w.requests, w.n_heads, w.head_dim, kvn, e["k_pre"], e["v_pre"])
     got = gw.cache.cpu().numpy()
     assert got.size >= img.size
@@ -53,7 +53,7 @@ def _full_wave_check(x, dev, kv, steps=1):
         ref_den = np.concatenate(oracle_rows(w, L.CALL_DENOISE, e, rows, kv))
         bar = (BF16_MAXABS, BF16_RELRMS) if kv == "bf16" else (FP8_MAXABS, FP8_RELRMS)
         check(f64(o_img[s]), ref_den, *bar, "denoise step %d" % s)
-        if kv == "fp8":   # also report against the unquantised prefix (not gated)
+        if kv != "bf16":   # also report against the unquantised prefix (not gated)
             ma, rr = errors(f64(o_img[s]), np.concatenate(oracle_rows(w, L.CALL_DENOISE, e, rows)))
             say("  %-40s max-abs %.3e  rel-RMS %.3e" % ("(fp8 vs unquantised prefix)", ma, rr))
         rows = [list(range(n)) for n in w.total_lens]
@@ -90,7 +90,7 @@ RAGGED = [
 
 
 @pytest.mark.parametrize("d", [128, 64])
-@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "fp8_v"])
 @pytest.mark.parametrize("case", range(len(RAGGED)))
 def test_ragged_waves(gpu_device, case, kv, d):
     reqs, h = RAGGED[case]
@@ -189,6 +189,52 @@ def test_full_size_wave8_fp8(gpu_device, big):
             assert np.array_equal(got, codes), (r, kvi, hh)
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "fp8_v"])
+def test_full_size_ten_references(gpu_device, big, kv):
+    """The model's maximum of ten references (41,216 prefix tokens) with each cache type;
+    bf16 also runs the full recompute and checks that reuse is exact."""
+    x = big("edit10")
+    w = x.workload
+    gw = GpuWave(x, gpu_device, kv=kv)
+    o_pre = gw.build()
+    o_img = gw.denoise()
+    torch.cuda.synchronize()
+    e = exact_inputs(x)
+    bar = (BF16_MAXABS, BF16_RELRMS) if kv == "bf16" else (FP8_MAXABS, FP8_RELRMS)
+    _sampled(gw, e, L.CALL_DENOISE, o_img, kv, 24, 6, bar)
+    if kv != "bf16":   # quality against the unquantised prefix, reported only
+        rng = np.random.default_rng(6)
+        heads = [0, 7, 23]
+        rows = [sample_rows(bl, L.CALL_DENOISE, 128, rng, 24) for bl in w.requests]
+        ref = oracle_rows(w, L.CALL_DENOISE, e, rows, "bf16", heads)
+        got = [f64(o_img)[np.asarray(rows[0])][:, heads]]
+        ma, rr = errors(np.concatenate(got), np.concatenate(ref))
+        say("  %-40s max-abs %.3e  rel-RMS %.3e" % ("(%s vs unquantised prefix)" % kv, ma, rr))
+    if kv == "bf16":
+        _sampled(gw, e, L.CALL_PREFIX, o_pre, "bf16", 24, 7, bar)
+        o_all = gw.full()
+        torch.cuda.synchronize()
+        lp = w.prefix_lens[0]
+        assert torch.equal(o_all[lp:].view(torch.int16), o_img.view(torch.int16)), \
+            "denoise differs from full recompute"
+    else:
+        # cache bytes of one head, K and V, against the oracle's encoder
+        from oracle import fp8 as F
+        cache = gw.cache.cpu().numpy()
+        lp, hh, d = w.prefix_lens[0], 5, w.head_dim
+        k0, v0 = e["k_pre"][:, hh], e["v_pre"][:, hh]
+        vcodes, _ = F.quantize_slab(v0)
+        off = qi.qi_plan_cache_offset(gw.plan, 0, 1, hh, 0)
+        assert np.array_equal(cache[off:off + lp * d].reshape(lp, d), vcodes)
+        off = qi.qi_plan_cache_offset(gw.plan, 0, 0, hh, 0)
+        if kv == "fp8":
+            kcodes, _ = F.quantize_slab(k0)
+            assert np.array_equal(cache[off:off + lp * d].reshape(lp, d), kcodes)
+        else:
+            kb = cache[off:off + lp * d * 2].view("<u2").reshape(lp, d)
+            assert np.array_equal(kb, L.bf16_bits(k0))
+
+
 # ------------------------------------------------------------------ invariants
 
 def _hash(t):
@@ -227,7 +273,7 @@ def test_request_isolation(gpu_device):
         arr[o0:o0 + lens[1]] = -arr[o0:o0 + lens[1]] * 1.5
     outs = []
     for x in (x1, x2):
-        for kv in ("bf16", "fp8"):
+        for kv in ("bf16", "fp8", "fp8_v"):
             gw = GpuWave(x, gpu_device, kv=kv)
             p = gw.build()
             d = gw.denoise()
@@ -235,8 +281,8 @@ def test_request_isolation(gpu_device):
             torch.cuda.synchronize()
             outs.append((kv, [split(w, t.cpu().view(torch.int16).numpy(), k)
                               for t, k in ((p, "pre"), (d, "img"), (f, "all"))]))
-    for i in range(2):
-        (_, a), (_, b) = outs[i], outs[i + 2]
+    for i in range(3):
+        (_, a), (_, b) = outs[i], outs[i + 3]
         for call in range(3):
             assert np.array_equal(a[call][0], b[call][0]) and np.array_equal(a[call][2], b[call][2])
             assert not np.array_equal(a[call][1], b[call][1])

@@ -134,6 +134,8 @@ def test_workload_shapes_follow_the_pages(facts):
     assert all(b == ref_tokens for b in W["edit4"].requests[0][1:-1])
     assert len(W["edit4"].requests[0]) - 2 == facts["max_references_vllm_omni"]["value"]
     assert len(W["wave8"].requests) == facts["step_batch_max_num_seqs"]["value"]
+    assert len(W["edit10"].requests[0]) - 2 == facts["max_references_model"]["value"]
+    assert all(b == ref_tokens for b in W["edit10"].requests[0][1:-1])
     assert max(W["wave8"].n_refs) <= facts["max_references_vllm_omni"]["value"]
     assert all(w.steps == facts["denoising_steps"]["value"] for k, w in W.items() if k != "tiny")
     assert all(w.layers == facts["dit_layers"]["value"] for k, w in W.items() if k != "tiny")
