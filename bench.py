@@ -259,6 +259,12 @@ def main():
             extra[n] = measure(n, max(2, a.steps // 2), 1, a.layers, dev, with_full=(n == "edit4"))
             log("[bench] %s" % json.dumps(extra[n]))
         if a.extra:
+            # true CFG: both branches in one wave against the positive branch alone
+            for n in ("edit1", "cfg_edit1"):
+                extra[n] = measure(n, max(2, a.steps // 2), 1, a.layers, dev, with_build=False)
+                log("[bench] %s" % json.dumps(extra[n]))
+            extra["cfg_edit1"]["step_time_over_single_branch"] = (
+                extra["cfg_edit1"]["ms_per_step"] / extra["edit1"]["ms_per_step"])
             # ten references: ~2.4 GB of buffers per layer, so 8 layers
             for kv in ("bf16", "fp8", "fp8_v"):
                 key = "edit10" if kv == "bf16" else "edit10_" + kv

@@ -29,6 +29,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 WAVE8_TEXT = (445, 349, 293, 185, 202, 82, 97, 71)
+CFG_NEG_TEXT = 64   # tokens of a short negative prompt (the pages give no length)
 WAVE8_REFS = (0, 4, 3, 4, 2, 3, 4, 3)
 
 
@@ -76,6 +77,13 @@ WORKLOADS = {
                          note="2048x2048 edit with one reference, 128x128 latent"),
     "wave8": Workload("wave8", 4, 24, 128, _wave8_requests(), kv_dtype="fp8",
                       note="eight 1024x1024 requests at one phase, fp8 prefix cache"),
+    "edit1": Workload("edit1", 7, 24, 128, [[256, 4096, 4096]],
+                      note="1024x1024 edit with one reference"),
+    # true CFG: the negative-prompt branch is a second request of the wave with its own
+    # (shorter) text, the same reference and an image block of the same size
+    "cfg_edit1": Workload("cfg_edit1", 6, 24, 128, [[256, 4096, 4096], [CFG_NEG_TEXT, 4096, 4096]],
+                          note="1024x1024 edit with one reference under true CFG: positive "
+                               "and negative branch in one wave"),
     "edit10": Workload("edit10", 5, 24, 128, [[256] + [4096] * 10 + [4096]],
                        note="1024x1024 edit with ten references (the model's maximum), "
                             "41,216 prefix tokens"),
@@ -138,6 +146,31 @@ def generate(workload, steps=1, seed=None):
         out.q_img.append(np.concatenate(img[0], 0))
         out.k_img.append(np.concatenate(img[1], 0))
         out.v_img.append(np.concatenate(img[2], 0))
+    return out
+
+
+def cfg_pair(x: WaveInputs, neg_text=CFG_NEG_TEXT, seed=0):
+    """True-CFG wave from a one-request wave x (the positive branch): request 1 is the
+    negative branch with a freshly drawn text block of neg_text tokens, the same reference
+    blocks and the same image Q/K/V (the two branches see the same latents)."""
+    w = x.workload
+    assert len(w.requests) == 1
+    bl = list(w.requests[0])
+    nbl = [int(neg_text)] + bl[1:]
+    rng = np.random.default_rng(seed)
+    gam = rng.uniform(0.8, 1.2, (w.n_heads, w.head_dim)).astype(np.float32)
+    t0 = bl[0]
+    pre = []
+    for a in (x.q_pre, x.k_pre, x.v_pre):
+        neg = np.concatenate([rms_rows(rng, neg_text, gam), a[t0:]], 0)
+        pre.append(np.concatenate([a, neg], 0))
+    w2 = Workload(w.name + "+cfg", w.seed, w.n_heads, w.head_dim, [bl, nbl], kv_dtype=w.kv_dtype,
+                  steps=w.steps, layers=w.layers, note="true-CFG pair")
+    out = WaveInputs(w2, *pre)
+    for s in range(len(x.q_img)):
+        out.q_img.append(np.concatenate([x.q_img[s], x.q_img[s]], 0))
+        out.k_img.append(np.concatenate([x.k_img[s], x.k_img[s]], 0))
+        out.v_img.append(np.concatenate([x.v_img[s], x.v_img[s]], 0))
     return out
 
 

@@ -98,6 +98,21 @@ def test_ragged_waves(gpu_device, case, kv, d):
     _full_wave_check(x, gpu_device, kv)
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_true_cfg_pair(gpu_device, kv):
+    """True CFG: the negative-prompt branch runs as a second request of the wave, with its
+    own text, the same reference and the same image Q/K/V (vLLM recipe "Qwen/Qwen-Image-2.1",
+    section "Sampling defaults": a negative prompt runs the DiT twice per step).  Both
+    branches match the oracle; the negative prompt changes the image rows."""
+    x = synth.custom([[150, 300, 400]], 3, 128, kv_dtype=kv, seed=41)
+    y = synth.cfg_pair(x, 40, seed=42)
+    gw = _full_wave_check(y, gpu_device, kv)
+    o = gw.denoise()
+    torch.cuda.synchronize()
+    pos, neg = split(y.workload, f64(o), "img")
+    assert pos.shape == neg.shape and not np.array_equal(pos, neg)
+
+
 # ------------------------------------------------------------------ full-size workloads
 
 @pytest.fixture(scope="module")
