@@ -82,24 +82,21 @@ struct Cfg {
   static constexpr int IPW = D / 32;         // 1 KiB direct V loads per wavefront per tile
   static constexpr int RPK = 512 / D;        // V rows per 1 KiB
   static_assert(PASS * ROWS == BN && IPW * RPK * 4 == BN, "tile shape");
-  // K tile: two halves of 32 rows; a row takes 2D bytes plus one spare 16-byte slot, so
-  // 16 consecutive rows start in 16 distinct bank groups (2D + 16 = 16 mod 256 for D=128,
-  // 144 for D=64; both generate all 16 slots) and a lane reads all of its row's chunks at
-  // one base address plus constant offsets.
-  static constexpr int KSTRIDE = 2 * D + 16;             // bytes per K row
-  static constexpr int KCH = KSTRIDE / 16;               // 16-byte slots per K row
-  static constexpr int KHALF_N = (32 * KCH + 63) / 64;   // 1 KiB loads per half
+  // K tile: rows of 2D bytes; logical 16-byte chunk c of row r sits at chunk c ^ ks(r), so
+  // the 16 consecutive rows one 16-byte MFMA-operand read touches (one chunk each) fall in
+  // 16 distinct bank groups.
+  static constexpr int KHALF_N = D / 16;                 // 1 KiB loads per 32-row half
   static constexpr int KHALF = KHALF_N * 1024;           // bytes per half
-  static constexpr int KTILE = KHALF;                    // bf16 elements per K tile (2 halves)
+  static constexpr int KTILE = BN * D;                   // bf16 elements per K tile
   static constexpr int VTILE = BN * D;                   // bf16 elements per V tile
+  static_assert(2 * KHALF == KTILE * 2, "two 32-row halves make a K tile");
+  __device__ static constexpr int ks(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
   // V tile: rows of 2D bytes; the 64-byte quarter q of row r sits at quarter q ^ vq(r), so
   // the transpose reads (32 lanes: 64 bytes of one quarter in each of 4 consecutive rows)
   // hit 64 distinct banks and a lane needs one base address per quarter.
   __device__ static constexpr int vq(int r) { return D == 128 ? (r & 3) : ((r >> 1) & 1); }
   // byte offsets of 16-byte chunk c of row r
-  __device__ static constexpr int koff(int r, int c) {
-    return (r >> 5) * KHALF + (r & 31) * KSTRIDE + c * 16;
-  }
+  __device__ static constexpr int koff(int r, int c) { return r * 2 * D + ((c ^ ks(r)) << 4); }
   __device__ static constexpr int voff(int r, int c) { return r * 2 * D + ((c ^ (vq(r) << 2)) << 4); }
 };
 
@@ -156,41 +153,38 @@ __device__ __forceinline__ int tile_kind(int kt, const TileArgs &a) {
 // Direct global -> LDS tile loads (bf16 sources).  Every load instruction fills 1 KiB of
 // LDS, lane l the 16 bytes at offset 16 l, so the layout is set on the global side: each
 // lane fetches the key row and chunk that belongs at its LDS slot.
-//   K: instruction i of half hf covers slots 64 i + l of that half; slot s holds row
-//      32 hf + s / KCH, chunk s % KCH; the spare slot of a row and the slots past the 32
-//      rows of a half take a copy of a real chunk of the half (never read).
-//   V: KiB kib holds rows kib * RPK + l / CH; physical chunk p of row r is logical chunk
-//      p ^ (vq(r) << 2) (vq depends on l only, as kib * RPK is a multiple of 4).
+//   K and V: KiB kib of a tile holds rows kib * RPK + l / CH; physical chunk p of row r is
+//      logical chunk p ^ ks(r) (K) or p ^ (vq(r) << 2) (V).  vq depends on l only (kib * RPK
+//      is a multiple of 4); ks on l and kib % 4 (D=128) or kib % 2 (D=64).
 // A group of four wavefronts loads either whole tiles (HALF = false) or one half of the
 // rows of each tile (HALF = true, the other group loads the other half); wavefront w of
-// the group issues the K instructions w, w + 4, ... and a run of consecutive V
-// instructions.  Instruction indices are wavefront-uniform, so the LDS destination is a
+// the group issues a run of consecutive K and V instructions.  Instruction indices are wavefront-uniform, so the LDS destination is a
 // scalar; the per-lane part of every global address is a 32-bit offset computed once,
 // added to a scalar base per tile.  Key tiles that straddle the cache/live boundary or
 // kend take a slower per-lane path.
 template <int D, int SRC, bool HALF>
 struct Direct {
   using C = Cfg<D>;
-  static constexpr int NIK = HALF ? C::KHALF_N : 2 * C::KHALF_N;   // K instructions loaded
-  static constexpr int NIV = HALF ? 2 * C::IPW : 4 * C::IPW;       // V instructions loaded
-  static constexpr int UK = (NIK + 3) / 4;                          // per wavefront, at most
-  static constexpr int UV = NIV / 4;                                // per wavefront
+  static constexpr int NI = HALF ? 2 * C::IPW : 4 * C::IPW;        // instructions per tensor
+  static constexpr int U = NI / 4;                                 // per wavefront
+  static constexpr int KP = D == 128 ? 4 : 2;   // K lane offsets repeat every KP instructions
   int w;                                  // wavefront index in the group (uniform)
-  uint32_t krow[UK], kch[UK];             // K: row in the tile (or half) and chunk, per load
+  uint32_t k_live[U], k_cache[U];         // K: lane offset from the instruction's first row
   uint32_t v_live, v_cache;               // V: lane offset from the instruction's first row
 
   __device__ __forceinline__ void init(const TileArgs &a) {
     w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 3;
     const int l = threadIdx.x & 63;
+    const int vr = l / C::CH;
 #pragma unroll
-    for (int u = 0; u < UK; ++u) {
-      const int j = 4 * u + w;
-      const int hf = HALF ? 0 : j / C::KHALF_N, i = HALF ? j : j % C::KHALF_N;
-      const int sl = 64 * i + l;
-      krow[u] = 32 * hf + min(sl / C::KCH, 31);
-      kch[u] = min(sl % C::KCH, C::CH - 1);
+    for (int u = 0; u < U; ++u) {
+      // instruction U w + u; only its residue mod KP matters (half offsets are multiples)
+      const int r = ((U * w + u) % KP) * C::RPK + vr;
+      const int kc = (l % C::CH) ^ C::ks(r);
+      k_live[u] = (uint32_t)(vr * a.H * D + kc * 8) * 2u;
+      k_cache[u] = (uint32_t)(vr * D + kc * 8) * 2u;
     }
-    const int vr = l / C::CH, vc = (l % C::CH) ^ (C::vq(vr) << 2);
+    const int vc = (l % C::CH) ^ (C::vq(vr) << 2);
     v_live = (uint32_t)(vr * a.H * D + vc * 8) * 2u;
     v_cache = (uint32_t)(vr * D + vc * 8) * 2u;
   }
@@ -218,41 +212,23 @@ struct Direct {
       const bool lv = kd == LIVE;
       const char *base = row_ptr(a, live, coff, k0);     // uniform
       const uint32_t rstride = lv ? a.H * D * 2 : D * 2;   // bytes between key rows
-      if (IS_K) {
 #pragma unroll
-        for (int u = 0; u < UK; ++u) {
-          const int j = 4 * u + w;
-          if (NIK % 4 != 0 && j >= NIK) break;
-          const int dst = (HALF ? hf * C::KHALF : (j / C::KHALF_N) * C::KHALF) + (j % C::KHALF_N) * 1024;
-          load(base + (krow[u] * rstride + kch[u] * 16), tile, dst);
-        }
-      } else {
-#pragma unroll
-        for (int u = 0; u < UV; ++u) {
-          const int ins = UV * w + u;   // V instruction within the loaded rows
-          const int dst = (HALF ? hf * (NIV * 1024) : 0) + ins * 1024;
-          load(base + (uint32_t)(ins * C::RPK) * rstride + (lv ? v_live : v_cache), tile, dst);
-        }
+      for (int u = 0; u < U; ++u) {
+        const int ins = U * w + u;   // instruction within the loaded rows
+        const int dst = (HALF ? hf * (NI * 1024) : 0) + ins * 1024;
+        const uint32_t lo = IS_K ? (lv ? k_live[u] : k_cache[u]) : (lv ? v_live : v_cache);
+        load(base + (uint32_t)(ins * C::RPK) * rstride + lo, tile, dst);
       }
     } else {
       // mixed sources or rows past kend (those load key kend - 1: finite values of this
       // request, masked later)
       const int l = threadIdx.x & 63;
 #pragma unroll
-      for (int u = 0; u < (IS_K ? UK : UV); ++u) {
-        int r, ch, dst;
-        if (IS_K) {
-          const int j = 4 * u + w;
-          if (NIK % 4 != 0 && j >= NIK) break;
-          r = krow[u];
-          ch = kch[u];
-          dst = (HALF ? hf * C::KHALF : (j / C::KHALF_N) * C::KHALF) + (j % C::KHALF_N) * 1024;
-        } else {
-          const int ins = UV * w + u;
-          r = ins * C::RPK + l / C::CH;
-          ch = (l % C::CH) ^ (C::vq(r) << 2);
-          dst = (HALF ? hf * (NIV * 1024) : 0) + ins * 1024;
-        }
+      for (int u = 0; u < U; ++u) {
+        const int ins = U * w + u;
+        const int r = ins * C::RPK + l / C::CH;
+        const int ch = (l % C::CH) ^ (IS_K ? C::ks(r) : (C::vq(r) << 2));
+        const int dst = (HALF ? hf * (NI * 1024) : 0) + ins * 1024;
         const int key = min(k0 + r, a.kend - 1);
         load(row_ptr(a, live, coff, key) + ch * 16, tile, dst);
       }
@@ -365,8 +341,8 @@ __device__ __forceinline__ void qk_tile(const __bf16 *Ks, const bf16x8_t (&qf)[C
   using C = Cfg<D>;
   const int lane = threadIdx.x & 63;
   const int j = lane & 31, g = lane >> 5;
-  // row j (+32 kb) of the tile, chunk 2 st + g
-  const char *kp = reinterpret_cast<const char *>(Ks) + C::koff(j, g);
+  // row j (+32 kb: same swizzle) of the tile, chunk 2 st + g
+  const char *kp = reinterpret_cast<const char *>(Ks) + j * 2 * D;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -375,8 +351,8 @@ __device__ __forceinline__ void qk_tile(const __bf16 *Ks, const bf16x8_t (&qf)[C
   for (int st = 0; st < C::QS; ++st) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const bf16x8_t a =
-          *reinterpret_cast<const bf16x8_t *>(kp + kb * C::KHALF + st * 32);
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(
+          kp + kb * C::KHALF + (((2 * st + g) ^ C::ks(j)) << 4));
       s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s[kb], 0, 0, 0);
     }
   }
