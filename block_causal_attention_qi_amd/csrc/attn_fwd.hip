@@ -65,6 +65,17 @@ constexpr int NT = 512;                 // ping-pong kernel: 8 wavefronts
 constexpr int NT_STAGED = 256;          // register-staged kernel: 4 wavefronts
 constexpr float TAU = 8.0f;   // lazy-rescale threshold, log2 units
 
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int SG_MFMA = 0x008, SG_DS_READ = 0x100;
+// MFMA operands read ahead of their MFMA in the MFMA phase
+#ifndef QI_QK_AHEAD
+#define QI_QK_AHEAD 4
+#endif
+#ifndef QI_PV_AHEAD
+#define QI_PV_AHEAD 2
+#endif
+constexpr int QK_AHEAD = QI_QK_AHEAD, PV_AHEAD = QI_PV_AHEAD;
+
 enum { SRC_ONE = 0, SRC_CACHE_BF16 = 1, SRC_CACHE_FP8 = 2, SRC_CACHE_FP8V = 3 };
 
 // Whether cached K (which = 0) or V (which = 1) rows are E4M3FN codes for a source kind.
@@ -356,6 +367,15 @@ __device__ __forceinline__ void qk_tile(const __bf16 *Ks, const bf16x8_t (&qf)[C
       s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s[kb], 0, 0, 0);
     }
   }
+  // schedule: four operand reads ahead, then one read per MFMA, so LDS latency hides
+  // behind the matrix core instead of stalling it
+  __builtin_amdgcn_sched_group_barrier(SG_DS_READ, QK_AHEAD, 0);
+#pragma unroll
+  for (int i = 0; i < 2 * C::QS - QK_AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(SG_MFMA, QK_AHEAD, 0);
 }
 
 // Mask the tail tile, take the row max, raise the running max when it is exceeded by
@@ -453,6 +473,14 @@ __device__ __forceinline__ void pv_tile(const __bf16 *Vs, const bf16x8_t (&p)[2]
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, both),
                                                          p[kb][cc], o[db], 0, 0, 0);
       }
+  // schedule: two MFMAs' operands (four transpose reads) ahead, then two reads per MFMA
+  __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2 * PV_AHEAD, 0);
+#pragma unroll
+  for (int i = 0; i < 4 * C::DB - PV_AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(SG_MFMA, PV_AHEAD, 0);
 }
 
 // ---------------------------------------------------------------------------------------
