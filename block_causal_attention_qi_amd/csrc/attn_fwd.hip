@@ -1,22 +1,20 @@
 // Block-causal attention forward for gfx950 (CDNA4), bf16 MFMA, fp32 online softmax.
 //
-// One workgroup owns one (request, head, row tile of <= 128 rows); each wavefront owns
-// 32 query rows and keeps its Q fragments and its O accumulator in registers for the
-// whole key loop.  Row tiles never cross a block, so
-// every row of a tile sees the same key prefix [0, kend) (block-causal rule: a row of
-// block b sees keys of blocks 0..b; ThakiCloud blog "Qwen-Image-2.1 vLLM-Omni day 0",
-// section "Serving architecture: the cross-step prefix KV cache").  Key tiles past kend
-// are never visited (EMPTY tiles skipped), the one straddling kend is masked (PARTIAL),
-// the others run unmasked (FULL).
+// One workgroup owns one (request, head, row tile); each wavefront owns 32 query rows and
+// keeps its Q fragments and its O accumulator in registers for the whole key loop.  Row
+// tiles never cross a block, so every row of a tile sees the same key prefix [0, kend)
+// (block-causal rule: a row of block b sees keys of blocks 0..b; ThakiCloud blog
+// "Qwen-Image-2.1 vLLM-Omni day 0", section "Serving architecture: the cross-step prefix
+// KV cache").  Key tiles past kend are never visited (EMPTY tiles skipped), the one
+// straddling kend is masked (PARTIAL), the others run unmasked (FULL).
 //
 // Key sources.  In the full and prefix calls K/V come from one token-major tensor.  In
 // the denoising call keys [0, lp) come from the prefix cache (head-major, bf16 or E4M3FN
-// codes with a per-head scale, dequantised while staging) and keys [lp, kend) from the
-// live image K/V; a key tile straddling lp gathers from both.  Key tiles start at key 0
-// in every call and the arithmetic does not depend on where a key came from, so on a
-// bf16 cache the denoising call reproduces the full call's image rows bit for bit -- the
-// exact reuse the vLLM recipe "Qwen/Qwen-Image-2.1" states in its "Prefix KV cache"
-// section.
+// codes with a per-head scale) and keys [lp, kend) from the live image K/V; a key tile
+// straddling lp gathers from both.  Key tiles start at key 0 in every call and the
+// arithmetic does not depend on where a key came from, so on a bf16 cache the denoising
+// call reproduces the full call's image rows bit for bit -- the exact reuse the vLLM
+// recipe "Qwen/Qwen-Image-2.1" states in its "Prefix KV cache" section.
 //
 // Per key tile (64 keys) and wavefront:
 //   S^T = K Q^T      16 x v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q in VGPRs)
@@ -34,16 +32,14 @@
 // cycle for 16-byte reads, 32 lanes per cycle for 8-byte reads).
 //
 // bf16 sources (full call, prefix call, denoising call on a bf16 cache): a workgroup of
-// 8 wavefronts (two per SIMD) owns 128 query rows; wavefronts w and w+4 hold the same 32
-// rows, and the two groups of four split the key tiles (group 0 the even ones, group 1
-// the odd ones).  The groups alternate phases ("ping-pong"): while one runs its MFMA
-// phase (QK^T of its tile j and PV of its tile j-2) the other runs its VALU phase
-// (softmax of its tile j-1) and loads its next tiles straight from global memory into
-// LDS (global_load_lds_dwordx4, no staging registers); the two swap at every workgroup
-// barrier, so each SIMD always has one wavefront feeding the matrix core and one feeding
-// the vector ALU.  At the end the two partial softmax states (m, l, O) of each row are
-// merged through LDS in a fixed order.  The fp8 cache is staged through registers,
-// where its codes are dequantised, by 4 wavefronts with a plain loop.
+// 8 wavefronts (two per SIMD) in two groups of four that alternate an MFMA phase and a
+// VALU phase (softmax, tile loads straight from global memory into LDS) between
+// workgroup barriers ("ping-pong"), so each SIMD always has one wavefront feeding the
+// matrix core and one feeding the vector ALU.  Row tiles of 256 rows give each wavefront
+// its own 32 rows; row tiles of 128 rows give two wavefronts the same rows, the two
+// groups split the key tiles, and the two partial softmax states are merged through LDS
+// in a fixed order.  The fp8 caches are staged through registers by 4 wavefronts with a
+// plain loop.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -138,6 +134,17 @@ __device__ __forceinline__ uint4 dequant8(uint32_t lo, uint32_t hi, float scale)
   r.y = pack_bf16(b[0] * scale, b[1] * scale);
   r.z = pack_bf16(c[0] * scale, c[1] * scale);
   r.w = pack_bf16(d[0] * scale, d[1] * scale);
+  return r;
+}
+
+// 8 E4M3FN codes -> 8 bf16 of the code values themselves (exact: every E4M3FN value is a
+// bf16 value; the scaled conversion with scale 1)
+__device__ __forceinline__ uint4 codes8(uint32_t lo, uint32_t hi) {
+  uint4 r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true));
+  r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false));
+  r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true));
   return r;
 }
 
@@ -249,8 +256,9 @@ struct Direct {
 
 // ---------------------------------------------------------------------------------------
 // Register-staged tile loads (fp8 caches): lane t stages chunk t % CH of rows
-// t / CH + i * ROWS (i < PASS) of both tiles and dequantises cached rows on the way (K
-// and V of the fp8 cache, V only of the V-only cache).
+// t / CH + i * ROWS (i < PASS) of both tiles.  Tiles wholly from the cache hold the code
+// values (exact in bf16) and the kernel applies the scales: K's folds into the logit
+// scale, V's into P.  Tiles mixing cached and live rows hold code * scale rounded to bf16.
 template <int D, int SRC>
 struct Stage {
   using C = Cfg<D>;
@@ -327,7 +335,10 @@ struct Stage {
     for (int i = 0; i < C::PASS; ++i) {
       const int r = row0 + i * C::ROWS;
       uint4 kv = kr[i], vv = vr[i];
-      if (kd == CACHED || (kd == MIXED && kt * BN + r < a.lp && kt * BN + r < a.kend)) {
+      if (kd == CACHED) {   // code values; the scales are applied in the softmax
+        if (coded(SRC, 0)) kv = codes8(kv.x, kv.y);
+        if (coded(SRC, 1)) vv = codes8(vv.x, vv.y);
+      } else if (kd == MIXED && kt * BN + r < a.lp && kt * BN + r < a.kend) {
         if (coded(SRC, 0)) kv = dequant8(kv.x, kv.y, a.k_scale);
         if (coded(SRC, 1)) vv = dequant8(vv.x, vv.y, a.v_scale);
       }
@@ -434,6 +445,31 @@ __device__ __forceinline__ void softmax_exp(const f32x16_t (&s)[2], float m_run,
       uint4 u = make_uint4(w[0], w[1], w[2], w[3]);
       p[kb][cc] = __builtin_bit_cast(bf16x8_t, u);
     }
+}
+
+// The same for a tile whose V rows hold code values that still need a scale vs: P holds
+// p * vs (2^(s c - m + log2 vs), so P V_codes = p V), the row sum adds p = (p * vs) / vs.
+__device__ __forceinline__ void softmax_exp_vscaled(const f32x16_t (&s)[2], float m_run, float c,
+                                                    float log2_vs, float inv_vs, float &l_run,
+                                                    bf16x8_t (&p)[2][2]) {
+  const float sh = log2_vs - m_run;
+  float lt = 0.0f;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      uint32_t w[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * cc + 2 * t], c, sh));
+        const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * cc + 2 * t + 1], c, sh));
+        w[t] = pack_bf16(x0, x1);
+        lt += x0 + x1;
+      }
+      uint4 u = make_uint4(w[0], w[1], w[2], w[3]);
+      p[kb][cc] = __builtin_bit_cast(bf16x8_t, u);
+    }
+  l_run = __builtin_fmaf(lt, inv_vs, l_run);
 }
 
 // O^T += V^T P^T.  V^T fragments by transpose reads: in each 16-lane group (i = lane %
@@ -797,6 +833,7 @@ __global__ __launch_bounds__(NT_STAGED, 2) void attn_staged_kernel(
   float m_run = -INFINITY, l_run = 0.0f;
 
   const int n = (tl.kend + BN - 1) / BN;
+  const float log2_vs = __builtin_log2f(a.v_scale), inv_vs = 1.0f / a.v_scale;
   Stage<D, SRC> st;
   st.init(a);
   st.load(0, a);
@@ -809,8 +846,12 @@ __global__ __launch_bounds__(NT_STAGED, 2) void attn_staged_kernel(
       f32x16_t s[2];
       bf16x8_t p[2][2];
       qk_tile<D>(lds[cur], qf, s);
-      softmax_max<D>(s, acc, m_run, l_run, j, tl.kend, c);
-      softmax_exp(s, m_run, c, l_run, p);
+      // tiles wholly from the cache hold code values: fold the scales in
+      const bool cached = tile_kind<SRC>(j, a) == CACHED;
+      const float ck = cached && coded(SRC, 0) ? c * a.k_scale : c;
+      const bool vs = cached && coded(SRC, 1);
+      softmax_max<D>(s, acc, m_run, l_run, j, tl.kend, ck);
+      softmax_exp_vscaled(s, m_run, ck, vs ? log2_vs : 0.0f, vs ? inv_vs : 1.0f, l_run, p);
       pv_tile<D>(lds[cur] + C::KTILE, p, acc);
     }
     if (j + 1 < n) st.store(j + 1, a, lds[cur ^ 1], lds[cur ^ 1] + C::KTILE);

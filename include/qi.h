@@ -39,7 +39,10 @@
  *   recipe section "Prefix KV cache").  Quantisation: per (request, head, K|V) a = max|x|
  *   over all prefix tokens and channels, scale = a/448, inv = 448/a (float32, correctly
  *   rounded; a == 0 gives 1 and 1), code = nearest E4M3FN value to the float32 product
- *   x*inv, ties to even, saturating at +-448.  Attention reads code*scale rounded to bf16.
+ *   x*inv, ties to even, saturating at +-448.  Attention uses the code values exactly (they
+ *   are bf16 values) with K's scale folded into the logit scale and V's into the
+ *   probabilities; on the one key tile of a request that mixes cached and live keys it
+ *   uses code*scale rounded to bf16.
  *
  * Ownership and errors.  The caller owns every device buffer (inputs, outputs, the
  * cache arena, the plan workspace) and the stream; the library owns only the host-side
