@@ -154,8 +154,10 @@ qi_status qi_plan_tile_map(const qi_plan *plan, int32_t call, int32_t bm, int32_
                            uint8_t *host_out, size_t n, size_t *n_needed);
 
 /* Tile shape (rows x keys) the attention kernel of a call uses; the tile map of the call
- * for this shape is the one the kernel follows (row tiles of the bf16-source kernel with
- * at most 128 rows additionally split their key tiles over two wavefront groups). */
+ * for this shape is the one the kernel follows.  To balance the last wave of workgroups
+ * the launch schedule may run a row tile as two halves of at most bm/2 rows each (the
+ * halves see the same key tiles, so the map is unchanged); the full call runs each row
+ * exactly as the prefix or denoising call runs it. */
 qi_status qi_plan_kernel_tile(const qi_plan *plan, int32_t call, int32_t *bm, int32_t *bn);
 
 /* Byte offset in the cache arena of element (request, kv = 0 K | 1 V, head, token,
