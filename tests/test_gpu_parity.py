@@ -334,6 +334,33 @@ def test_closed_forms_on_gpu(gpu_device):
     check(f64(o), np.stack(ref), BF16_MAXABS, BF16_RELRMS, "constant K -> mean of V")
 
 
+@pytest.mark.parametrize("kv", ["fp8", "fp8_v"])
+def test_fp8_zero_head(gpu_device, kv):
+    """A head whose prefix K and V are all zero has absmax 0: its scales are 1 and its
+    codes 0 (the quantiser's a == 0 case), and the denoising step still matches the oracle
+    on every row; a head with tiny values keeps its relative precision."""
+    reqs = [[64, 150, 200], [40, 128]]
+    x = synth.custom(reqs, 3, 128, kv_dtype=kv, seed=12)
+    x.k_pre[:, 1] = 0.0
+    x.v_pre[:, 1] = 0.0
+    x.v_pre[:, 2] *= 1e-6
+    _full_wave_check(x, gpu_device, kv)
+    gw = GpuWave(x, gpu_device, kv=kv)
+    gw.build()
+    torch.cuda.synchronize()
+    cache = gw.cache.cpu().numpy()
+    for r in range(len(reqs)):
+        s_off = qi.qi_plan_cache_offset(gw.plan, r, 2, 0, 0)
+        sc = cache[s_off:s_off + 8 * 3].view("<f4").reshape(2, 3)
+        assert sc[0, 1] == 1.0 and sc[1, 1] == 1.0
+        off = qi.qi_plan_cache_offset(gw.plan, r, 1, 1, 0)
+        assert not cache[off:off + w_lp(reqs[r]) * 128].any()
+
+
+def w_lp(bl):
+    return int(sum(bl[:-1]))
+
+
 # ------------------------------------------------------------------ errors on device
 
 def test_error_paths_leave_outputs_untouched(gpu_device):
