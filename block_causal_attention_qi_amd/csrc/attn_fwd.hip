@@ -541,6 +541,38 @@ __device__ __forceinline__ void load_q(const __bf16 *q, const qi_tile &tl, int H
   }
 }
 
+// Q through LDS: the wavefront loads its 32 rows (row0 .. row0 + 31 of the tile) straight
+// into `stage` with whole rows per load instruction (chunks placed as in a K tile; rows
+// past the tile repeat its last row, finite and never stored), waits, and reads its
+// MFMA B fragments back: qf[st] holds dims 16 st + 8 g .. + 7 of row j (lane = j + 32 g).
+// `stage` must be wavefront-uniform and touched by no other wavefront meanwhile.
+template <int D>
+__device__ __forceinline__ void issue_q_lds(const __bf16 *q, const qi_tile &tl, int H, int h,
+                                            int row0, __bf16 *stage) {
+  using C = Cfg<D>;
+  constexpr int RPI = 64 / C::CH;   // rows per 64-lane instruction
+  const int lane = threadIdx.x & 63;
+  const int c = lane % C::CH;
+#pragma unroll
+  for (int it = 0; it < 32 / RPI; ++it) {
+    const int r = it * RPI + lane / C::CH;
+    const int tr = min(row0 + r, tl.nrows - 1);
+    const __bf16 *src = q + ((int64_t)(tl.q_tok + tr) * H + h) * D + 8 * (c ^ C::ks(r));
+    __builtin_amdgcn_global_load_lds(src, (lds_void_t *)(reinterpret_cast<char *>(stage) + it * 1024),
+                                     16, 0, 0);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void read_q_lds(const __bf16 *stage, bf16x8_t (&qf)[Cfg<D>::QS]) {
+  using C = Cfg<D>;
+  const int lane = threadIdx.x & 63;
+  const char *sb = reinterpret_cast<const char *>(stage);
+#pragma unroll
+  for (int st = 0; st < C::QS; ++st)
+    qf[st] = *reinterpret_cast<const bf16x8_t *>(sb + C::koff(lane & 31, 2 * st + (lane >> 5)));
+}
+
 template <int D>
 __device__ __forceinline__ void store_o(__bf16 *o, const qi_tile &tl, int H, int h, int row,
                                         const f32x16_t (&acc)[Cfg<D>::DB], float l_run) {
@@ -559,6 +591,41 @@ __device__ __forceinline__ void store_o(__bf16 *o, const qi_tile &tl, int H, int
       u.y = pack_bf16(acc[db][4 * aa + 2] * inv, acc[db][4 * aa + 3] * inv);
       *reinterpret_cast<uint2 *>(op + dim) = u;
     }
+}
+
+// The same result written through LDS: the wavefront puts its 32 normalised rows into
+// `stage` (32 rows of 2D bytes, chunks placed as in a K tile, so both the 8-byte writes
+// and the 16-byte reads are free of bank conflicts) and reads them back row by row, so
+// every global store instruction writes whole rows (64 lanes x 16 bytes) instead of 16
+// bytes in each of 32 rows.  row0: the wavefront's first row in the tile.  Only this
+// wavefront touches `stage`.
+template <int D>
+__device__ __forceinline__ void store_o_lds(__bf16 *o, const qi_tile &tl, int H, int h, int row0,
+                                            const f32x16_t (&acc)[Cfg<D>::DB], float l_run,
+                                            __bf16 *stage) {
+  using C = Cfg<D>;
+  const int lane = threadIdx.x & 63;
+  const int j = lane & 31, g = lane >> 5;
+  const float inv = 1.0f / pair_sum(l_run);
+  char *sb = reinterpret_cast<char *>(stage);
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int aa = 0; aa < 4; ++aa) {
+      uint2 u;   // dims 32 db + 8 aa + 4 g .. + 3 of row j: half g of chunk 4 db + aa
+      u.x = pack_bf16(acc[db][4 * aa] * inv, acc[db][4 * aa + 1] * inv);
+      u.y = pack_bf16(acc[db][4 * aa + 2] * inv, acc[db][4 * aa + 3] * inv);
+      *reinterpret_cast<uint2 *>(sb + C::koff(j, 4 * db + aa) + 8 * g) = u;
+    }
+  constexpr int RPI = 64 / C::CH;   // rows per 64-lane instruction
+  const int c = lane % C::CH;
+#pragma unroll
+  for (int it = 0; it < 32 / RPI; ++it) {
+    const int r = it * RPI + lane / C::CH;
+    const uint4 u = *reinterpret_cast<const uint4 *>(sb + C::koff(r, c));
+    if (row0 + r < tl.nrows)
+      *reinterpret_cast<uint4 *>(o + ((int64_t)(tl.q_tok + row0 + r) * H + h) * D + 8 * c) = u;
+  }
 }
 
 __device__ __forceinline__ TileArgs make_args(const qi_tile &tl, int H, int h, const __bf16 *k,
@@ -601,6 +668,26 @@ struct Ring {
 #define QI_RING(r, arr, i) \
   ((i) == 0 ? (r).arr##0 : (i) == 1 ? (r).arr##1 : (i) == 2 ? (r).arr##2 : (r).arr##3)
 
+// K slot i for a wavefront-uniform run-time i.  Selects of pointer values, not of the
+// members' addresses: the ring must stay in registers, since the backend cannot emit a
+// memory copy of LDS addresses.
+__device__ __forceinline__ __bf16 *pick4(int i, __bf16 *p0, __bf16 *p1, __bf16 *p2, __bf16 *p3) {
+  __bf16 *const lo = (i & 1) ? p1 : p0;
+  __bf16 *const hi = (i & 1) ? p3 : p2;
+  return (i & 2) ? hi : lo;
+}
+__device__ __forceinline__ __bf16 *ring_k(const Ring &r, int i) {
+  return pick4(i, r.K0, r.K1, r.K2, r.K3);
+}
+
+// Q staging before the key loop: wavefront w uses half w & 1 of slot K3, V1, V2 or V3
+// (w >> 1), the slots the prologue leaves free.
+template <int D>
+__device__ __forceinline__ __bf16 *q_stage(const Ring &r) {
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  return pick4(w >> 1, r.K3, r.V1, r.V2, r.V3) + (w & 1) * 32 * D;
+}
+
 // Row tiles of more than 128 rows: wavefront w owns rows 32w..32w+31 and every key tile
 // is read by all eight wavefronts (group 0 = waves 0..3, group 1 = waves 4..7).
 //   period 2t:   group 0 MFMA phase t: S = QK^T(K_t) (t < n), O += PV(V_{t-1}) (t >= 1)
@@ -608,9 +695,12 @@ struct Ring {
 //                                     K_{t+2}, V_{t+1} (t >= 1)
 //   period 2t+1: group 1 MFMA phase t; group 0 VALU phase: P = softmax(tile t); waits;
 //                                     loads its halves of K_{t+3}, V_{t+2}
-// Group g loads half g of each tile's rows.  K_0..K_2 and V_0, V_1 are loaded before
-// period 0.  A half tile issued in period p is waited for at the end of p+2 and first read
-// in period >= p+4; the slots it overwrites (K_{m-4}, V_{m-4}) were last read in p-1.
+// Group g loads half g of each tile's rows.  K_0..K_2 and V_0 are loaded before period 0,
+// together with each wavefront's Q rows, staged in the slots still free (K3, V1..V3);
+// V_1 follows once every Q stage has been read: group 1 loads its half in period 0, group
+// 0 in period 1.  A half tile issued in period p is waited for at the end of p+2 and first
+// read in period >= p+3 (>= p+4 in the steady state); the slots it overwrites (K_{m-4},
+// V_{m-4}) were last read in p-1.
 template <int D, int SRC>
 __device__ __forceinline__ void pp_rows256(const Ring &r, const qi_tile &tl, int H, int h,
                                            const TileArgs &a, const __bf16 *q, __bf16 *o,
@@ -618,28 +708,27 @@ __device__ __forceinline__ void pp_rows256(const Ring &r, const qi_tile &tl, int
   using C = Cfg<D>;
   const int wave = threadIdx.x >> 6;
   const int group = wave >> 2;
-  const int row = wave * 32 + (threadIdx.x & 31);
   const bool active = wave * 32 < tl.nrows;   // the wavefront's rows exist
 
-  bf16x8_t qf[C::QS];
-  load_q<D>(q, tl, H, h, row, qf);
+  const int n = (tl.kend + BN - 1) / BN;
+  Direct<D, SRC, true> dm;
+  dm.init(a);
+  __bf16 *const qst = q_stage<D>(r);
+  issue_q_lds<D>(q, tl, H, h, wave * 32, qst);
+  dm.template issue<true>(0, a, a.k, a.k_off, r.K0, group);
+  if (n > 1) dm.template issue<true>(1, a, a.k, a.k_off, r.K1, group);
+  if (n > 2) dm.template issue<true>(2, a, a.k, a.k_off, r.K2, group);
+  dm.template issue<false>(0, a, a.v, a.v_off, r.V0, group);
   f32x16_t acc[C::DB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) acc[db][rr] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
-
-  const int n = (tl.kend + BN - 1) / BN;
-  Direct<D, SRC, true> dm;
-  dm.init(a);
-  dm.template issue<true>(0, a, a.k, a.k_off, r.K0, group);
-  if (n > 1) dm.template issue<true>(1, a, a.k, a.k_off, r.K1, group);
-  if (n > 2) dm.template issue<true>(2, a, a.k, a.k_off, r.K2, group);
-  dm.template issue<false>(0, a, a.v, a.v_off, r.V0, group);
-  if (n > 1) dm.template issue<false>(1, a, a.v, a.v_off, r.V1, group);
   __builtin_amdgcn_s_waitcnt(0);
-  bar();
+  bf16x8_t qf[C::QS];
+  read_q_lds<D>(qst, qf);
+  bar();   // every Q stage read: V1 may be loaded (group 1 in period 0, group 0 in period 1)
 
   f32x16_t s[2];
   bf16x8_t p[2][2];
@@ -663,7 +752,7 @@ __device__ __forceinline__ void pp_rows256(const Ring &r, const qi_tile &tl, int
       }
       __builtin_amdgcn_s_waitcnt(0);
       if (t >= 1 && t + 2 < n) dm.template issue<true>(t + 2, a, a.k, a.k_off, QI_RING(r, K, (T + 2) & 3), 1);
-      if (t >= 1 && t + 1 < n) dm.template issue<false>(t + 1, a, a.v, a.v_off, QI_RING(r, V, (T + 1) & 3), 1);
+      if (t + 1 < n) dm.template issue<false>(t + 1, a, a.v, a.v_off, QI_RING(r, V, (T + 1) & 3), 1);
     }
     bar();
     // period 2t+1
@@ -677,6 +766,7 @@ __device__ __forceinline__ void pp_rows256(const Ring &r, const qi_tile &tl, int
       __builtin_amdgcn_s_waitcnt(0);
       if (t + 3 < n) dm.template issue<true>(t + 3, a, a.k, a.k_off, QI_RING(r, K, (T + 3) & 3), 0);
       if (t + 2 < n) dm.template issue<false>(t + 2, a, a.v, a.v_off, QI_RING(r, V, (T + 2) & 3), 0);
+      if (T == 0 && t == 0 && n > 1) dm.template issue<false>(1, a, a.v, a.v_off, r.V1, 0);
     }
     bar();
   };
@@ -686,7 +776,11 @@ __device__ __forceinline__ void pp_rows256(const Ring &r, const qi_tile &tl, int
     if (t0 + 2 <= n) tile(Slot<2>(), t0 + 2);
     if (t0 + 3 <= n) tile(Slot<3>(), t0 + 3);
   }
-  if (active) store_o<D>(o, tl, H, h, row, acc, l_run);
+  // the ring is free: every load was waited for and every read consumed before the last
+  // barrier; wavefront w stages its rows in half w & 1 of K slot w >> 1
+  if (active)
+    store_o_lds<D>(o, tl, H, h, wave * 32, acc, l_run,
+                   ring_k(r, wave >> 1) + (wave & 1) * 32 * D);
 }
 
 // Row tiles of at most 128 rows: wavefronts w and w+4 hold the same 32 rows and the two
@@ -696,8 +790,9 @@ __device__ __forceinline__ void pp_rows256(const Ring &r, const qi_tile &tl, int
 //                             loads of two periods ago; loads K_{p+3}, V_{p+1} (its own
 //                             MFMA phase reads them in period p+3), overwriting K_{p-1}
 //                             and V_{p-3}, last read in period p-1.
-// K_0, K_1, K_2 and V_0 are loaded before period 0.  Afterwards group 1 stores its
-// (m, l, O) in LDS and group 0 merges them into its own (fixed order).
+// K_0, K_1, K_2 and V_0 are loaded before period 0, with every wavefront's copy of its Q
+// rows staged in K3, V1..V3.  Afterwards group 1 stores its (m, l, O) in LDS and group 0
+// merges them into its own (fixed order).
 template <int D, int SRC>
 __device__ __forceinline__ void pp_rows128(const Ring &r, const qi_tile &tl, int H, int h,
                                            const TileArgs &a, const __bf16 *q, __bf16 *o,
@@ -705,27 +800,27 @@ __device__ __forceinline__ void pp_rows128(const Ring &r, const qi_tile &tl, int
   using C = Cfg<D>;
   const int wave = threadIdx.x >> 6;
   const int group = wave >> 2;
-  const int row = (wave & 3) * 32 + (threadIdx.x & 31);
   const bool active = (wave & 3) * 32 < tl.nrows;   // the wavefront's rows exist
 
-  bf16x8_t qf[C::QS];
-  load_q<D>(q, tl, H, h, row, qf);
+  const int n = (tl.kend + BN - 1) / BN;
+  Direct<D, SRC, false> dm;
+  dm.init(a);
+  __bf16 *const qst = q_stage<D>(r);   // both groups load their copy of the rows
+  issue_q_lds<D>(q, tl, H, h, (wave & 3) * 32, qst);
+  if (group == 0) dm.template issue<true>(0, a, a.k, a.k_off, r.K0);
+  if (group == 1 && n > 1) dm.template issue<true>(1, a, a.k, a.k_off, r.K1);
+  if (group == 0 && n > 2) dm.template issue<true>(2, a, a.k, a.k_off, r.K2);
+  if (group == 1) dm.template issue<false>(0, a, a.v, a.v_off, r.V0);
   f32x16_t acc[C::DB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) acc[db][rr] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
-
-  const int n = (tl.kend + BN - 1) / BN;
-  Direct<D, SRC, false> dm;
-  dm.init(a);
-  if (group == 0) dm.template issue<true>(0, a, a.k, a.k_off, r.K0);
-  if (group == 1 && n > 1) dm.template issue<true>(1, a, a.k, a.k_off, r.K1);
-  if (group == 0 && n > 2) dm.template issue<true>(2, a, a.k, a.k_off, r.K2);
-  if (group == 1) dm.template issue<false>(0, a, a.v, a.v_off, r.V0);
   __builtin_amdgcn_s_waitcnt(0);
-  bar();
+  bf16x8_t qf[C::QS];
+  read_q_lds<D>(qst, qf);
+  bar();   // every Q stage read: its slots may be loaded
 
   f32x16_t s[2];
   bf16x8_t p[2][2];
@@ -759,7 +854,7 @@ __device__ __forceinline__ void pp_rows128(const Ring &r, const qi_tile &tl, int
   // merge the two partial states of each row (group 1 -> LDS -> group 0); the ring is
   // free: every load was waited for and every read consumed
   const int w4 = wave & 3, lane = threadIdx.x & 63;
-  float *ost = reinterpret_cast<float *>(QI_RING(r, K, w4)) + lane;
+  float *ost = reinterpret_cast<float *>(ring_k(r, w4)) + lane;
   float *mst = reinterpret_cast<float *>(r.V0) + (w4 * 64 + lane) * 2;
   if (group == 1 && active) {
 #pragma unroll
@@ -780,7 +875,8 @@ __device__ __forceinline__ void pp_rows128(const Ring &r, const qi_tile &tl, int
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) acc[db][rr] = acc[db][rr] * a0 + ost[(16 * db + rr) * 64] * a1;
     l_run = l_run * a0 + l1 * a1;
-    store_o<D>(o, tl, H, h, row, acc, l_run);
+    // stage in this wavefront's own merge buffer, whose values are now in registers
+    store_o_lds<D>(o, tl, H, h, w4 * 32, acc, l_run, ring_k(r, w4));
   }
 }
 
