@@ -354,6 +354,10 @@ struct Stage {
 // LDS accesses across it; every LDS read before it has been consumed by an MFMA.
 __device__ __forceinline__ void bar() { asm volatile("s_barrier" ::: "memory"); }
 
+// Wait for this wavefront's LDS operations only (gfx9 s_waitcnt encoding: lgkmcnt 0,
+// vmcnt (bits 3:0, 15:14) and expcnt (6:4) at their maxima).
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14)); }
+
 // ---------------------------------------------------------------------------------------
 // Per-wavefront pieces of one key tile.
 
@@ -728,6 +732,7 @@ __device__ __forceinline__ void pp_rows256(const Ring &r, const qi_tile &tl, int
   __builtin_amdgcn_s_waitcnt(0);
   bf16x8_t qf[C::QS];
   read_q_lds<D>(qst, qf);
+  wait_lds();
   bar();   // every Q stage read: V1 may be loaded (group 1 in period 0, group 0 in period 1)
 
   f32x16_t s[2];
@@ -820,6 +825,7 @@ __device__ __forceinline__ void pp_rows128(const Ring &r, const qi_tile &tl, int
   __builtin_amdgcn_s_waitcnt(0);
   bf16x8_t qf[C::QS];
   read_q_lds<D>(qst, qf);
+  wait_lds();
   bar();   // every Q stage read: its slots may be loaded
 
   f32x16_t s[2];
