@@ -526,25 +526,6 @@ __device__ __forceinline__ void pv_tile(const __bf16 *Vs, const bf16x8_t (&p)[2]
 // ---------------------------------------------------------------------------------------
 // Common prologue / epilogue.
 
-struct Work {
-  qi_tile tl;
-  int h;
-};
-
-// row: this lane's query row inside the tile (lanes j and j + 32 share one row)
-template <int D>
-__device__ __forceinline__ void load_q(const __bf16 *q, const qi_tile &tl, int H, int h, int row,
-                                       bf16x8_t (&qf)[Cfg<D>::QS]) {
-  const int lane = threadIdx.x & 63;
-  const bool valid = row < tl.nrows;
-  const __bf16 *qp = q + ((int64_t)(tl.q_tok + row) * H + h) * D + 8 * (lane >> 5);
-#pragma unroll
-  for (int st = 0; st < Cfg<D>::QS; ++st) {
-    uint4 u = valid ? *reinterpret_cast<const uint4 *>(qp + 16 * st) : make_uint4(0, 0, 0, 0);
-    qf[st] = __builtin_bit_cast(bf16x8_t, u);
-  }
-}
-
 // Q through LDS: the wavefront loads its 32 rows (row0 .. row0 + 31 of the tile) straight
 // into `stage` with whole rows per load instruction (chunks placed as in a K tile; rows
 // past the tile repeat its last row, finite and never stored), waits, and reads its
@@ -577,6 +558,7 @@ __device__ __forceinline__ void read_q_lds(const __bf16 *stage, bf16x8_t (&qf)[C
     qf[st] = *reinterpret_cast<const bf16x8_t *>(sb + C::koff(lane & 31, 2 * st + (lane >> 5)));
 }
 
+// O straight from the accumulators: lane (j, g) writes 8 bytes of row j per instruction.
 template <int D>
 __device__ __forceinline__ void store_o(__bf16 *o, const qi_tile &tl, int H, int h, int row,
                                         const f32x16_t (&acc)[Cfg<D>::DB], float l_run) {
@@ -597,12 +579,12 @@ __device__ __forceinline__ void store_o(__bf16 *o, const qi_tile &tl, int H, int
     }
 }
 
-// The same result written through LDS: the wavefront puts its 32 normalised rows into
-// `stage` (32 rows of 2D bytes, chunks placed as in a K tile, so both the 8-byte writes
-// and the 16-byte reads are free of bank conflicts) and reads them back row by row, so
-// every global store instruction writes whole rows (64 lanes x 16 bytes) instead of 16
-// bytes in each of 32 rows.  row0: the wavefront's first row in the tile.  Only this
-// wavefront touches `stage`.
+// O through LDS: the wavefront normalises its 32 rows (O / l, rounded to bf16), writes
+// them into `stage` (32 rows of 2D bytes, chunks placed as in a K tile, so both the
+// 8-byte writes and the 16-byte reads are free of bank conflicts) and reads them back row
+// by row, so every global store instruction writes whole rows (64 lanes x 16 bytes)
+// rather than 16 bytes in each of 32 rows.  row0: the wavefront's first row in the tile;
+// rows past the tile are not stored.  Only this wavefront touches `stage`.
 template <int D>
 __device__ __forceinline__ void store_o_lds(__bf16 *o, const qi_tile &tl, int H, int h, int row0,
                                             const f32x16_t (&acc)[Cfg<D>::DB], float l_run,
@@ -922,11 +904,12 @@ __global__ __launch_bounds__(NT_STAGED, 2) void attn_staged_kernel(
   const qi_tile tl = tiles[item / H];
   const int h = item % H;
   const TileArgs a = make_args(tl, H, h, k, v, cache, SRC == SRC_CACHE_FP8 || SRC == SRC_CACHE_FP8V);
-  const int row = (threadIdx.x >> 6) * 32 + (threadIdx.x & 31);
-  const bool active = (threadIdx.x >> 6) * 32 < tl.nrows;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool active = wave * 32 < tl.nrows;
 
-  bf16x8_t qf[C::QS];
-  load_q<D>(q, tl, H, h, row, qf);
+  // Q rows staged in buffer 1 (8 KiB per wavefront), free until tile 1 is stored
+  __bf16 *const qst = lds[1] + wave * 32 * D;
+  issue_q_lds<D>(q, tl, H, h, wave * 32, qst);
   f32x16_t acc[C::DB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
@@ -940,6 +923,9 @@ __global__ __launch_bounds__(NT_STAGED, 2) void attn_staged_kernel(
   st.init(a);
   st.load(0, a);
   st.store(0, a, lds[0], lds[0] + C::KTILE);
+  __builtin_amdgcn_s_waitcnt(0);
+  bf16x8_t qf[C::QS];
+  read_q_lds<D>(qst, qf);
   if (n > 1) st.load(1, a);
   __syncthreads();
   for (int j = 0; j < n; ++j) {
@@ -960,7 +946,9 @@ __global__ __launch_bounds__(NT_STAGED, 2) void attn_staged_kernel(
     if (j + 2 < n) st.load(j + 2, a);
     __syncthreads();
   }
-  if (active) store_o<D>(o, tl, H, h, row, acc, l_run);
+  // (two workgroups share a CU here, so the other one computes while this one stores:
+  // staging O through LDS measured no faster, and costs registers)
+  if (active) store_o<D>(o, tl, H, h, wave * 32 + (threadIdx.x & 31), acc, l_run);
 }
 
 template <int D, int SRC>
