@@ -82,6 +82,21 @@ def test_brute_force_tiny_all_calls(tiny):
     assert np.max(np.abs(got - ref)) <= 1e-12
 
 
+def test_brute_force_tiny_float32_rows(tiny):
+    """The tiny case as drawn, in float32 (widened exactly to float64), before any rounding
+    to bf16: the full step and the last denoising step against the brute force."""
+    w, x = tiny
+    bl = w.requests[0]
+    lp = w.prefix_lens[0]
+    qa, ka, va = (np.asarray(t, dtype=np.float64) for t in x.full(2))
+    assert x.q_pre.dtype == np.float32
+    got = A.full_step(bl, qa, ka, va)[:, 0, :]
+    ref = _brute_attention(bl, range(len(qa)), qa[:, 0].tolist(), ka[:, 0].tolist(), va[:, 0].tolist())
+    assert np.max(np.abs(got - ref)) <= 1e-12
+    got = A.denoise_step(bl, qa[lp:], ka[:lp], va[:lp], ka[lp:], va[lp:])[:, 0, :]
+    assert np.max(np.abs(got - ref[lp:])) <= 1e-12
+
+
 # ---------------------------------------------------------------- library special cases
 
 def _sdpa(q, k, v, causal):
