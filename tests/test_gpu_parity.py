@@ -98,6 +98,30 @@ def test_ragged_waves(gpu_device, case, kv, d):
     _full_wave_check(x, gpu_device, kv)
 
 
+def _max_wave(seed):
+    """QI_MAX_REQUESTS requests with 0..QI_MAX_REFS references each (every count present)
+    and short ragged blocks (1..40 tokens)."""
+    rng = np.random.default_rng(seed)
+    reqs = []
+    for r in range(qi.QI_MAX_REQUESTS):
+        n_refs = r % (qi.QI_MAX_REFS + 1)
+        reqs.append([int(x) for x in rng.integers(1, 41, size=n_refs + 2)])
+    return reqs
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_maximum_wave(gpu_device, kv):
+    x = synth.custom(_max_wave(77), 2, 128, kv_dtype=kv, seed=77)
+    assert len(x.workload.requests) == qi.QI_MAX_REQUESTS
+    _full_wave_check(x, gpu_device, kv)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_maximum_heads(gpu_device, d):
+    x = synth.custom([[20, 33, 47], [3, 200]], qi.QI_MAX_HEADS, d, seed=78)
+    _full_wave_check(x, gpu_device, "bf16")
+
+
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
 def test_true_cfg_pair(gpu_device, kv):
     """True CFG: the negative-prompt branch runs as a second request of the wave, with its
