@@ -393,39 +393,56 @@ __device__ __forceinline__ void qk_tile(const __bf16 *Ks, const bf16x8_t (&qf)[C
   __builtin_amdgcn_sched_group_barrier(SG_MFMA, QK_AHEAD, 0);
 }
 
-// Mask the tail tile, take the row max, raise the running max when it is exceeded by
-// more than TAU (rescaling O and l exactly).
-template <int D>
-__device__ __forceinline__ void softmax_max(f32x16_t (&s)[2], f32x16_t (&o)[Cfg<D>::DB],
-                                            float &m_run, float &l_run, int kt, int kend,
-                                            float c) {
-  using C = Cfg<D>;
+// Keys at or past kend of the PARTIAL tile kt get score -inf.
+__device__ __forceinline__ void mask_tile(f32x16_t (&s)[2], int kt, int kend) {
   const int g = (threadIdx.x & 63) >> 5;
-  if ((kt + 1) * BN > kend) {   // the PARTIAL tile: keys at or past kend do not exist
+  // score (kb, r) of this lane is key kt BN + 32 kb + 8 (r / 4) + 4 g + r % 4: compare the
+  // constant part against one per-lane limit
+  const int lim = kend - kt * BN - 4 * g;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+  for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kt * BN + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (key >= kend) s[kb][r] = -INFINITY;
-      }
-  }
+    for (int r = 0; r < 16; ++r)
+      if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) s[kb][r] = -INFINITY;
+}
+
+// c times the row max of a tile's scores (both lanes of the row agree).  Taken before the
+// PARTIAL tile is masked: its key rows past kend hold copies of key kend - 1 (see Direct),
+// whose score is already in the row, so they cannot change the max.
+__device__ __forceinline__ float tile_max(const f32x16_t (&s)[2], float c) {
   float mx = s[0][0];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-  const float mc = pair_max(mx) * c;
+  return pair_max(mx) * c;
+}
+
+// Raise the running max to mc when some row of the wavefront exceeds it by more than TAU,
+// rescaling O and l exactly.
+template <int D>
+__device__ __forceinline__ void raise_max(f32x16_t (&o)[Cfg<D>::DB], float &m_run, float &l_run,
+                                          float mc) {
   if (__any(mc > m_run + TAU)) {
     const float mn = fmaxf(m_run, mc);
     const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
     m_run = mn;
     l_run *= alpha;
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
+    for (int db = 0; db < Cfg<D>::DB; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
   }
+}
+
+// Mask the tail tile, take the row max, raise the running max when it is exceeded by
+// more than TAU (rescaling O and l exactly).
+template <int D>
+__device__ __forceinline__ void softmax_max(f32x16_t (&s)[2], f32x16_t (&o)[Cfg<D>::DB],
+                                            float &m_run, float &l_run, int kt, int kend,
+                                            float c) {
+  if ((kt + 1) * BN > kend) mask_tile(s, kt, kend);   // the PARTIAL tile
+  raise_max<D>(o, m_run, l_run, tile_max(s, c));
 }
 
 // P = 2^(s c - m) in bf16, in the MFMA B-operand order: step (kb, cc) holds keys
@@ -476,11 +493,33 @@ __device__ __forceinline__ void softmax_exp_vscaled(const f32x16_t (&s)[2], floa
   l_run = __builtin_fmaf(lt, inv_vs, l_run);
 }
 
+// Instruction order of the PV block: two MFMAs' operands (four transpose reads) ahead, then
+// two reads and VS vector instructions (other work of the same basic block) per MFMA.
+constexpr int SG_VALU = 0x002;
+#ifndef QI_PV_VALU
+#define QI_PV_VALU 2
+#endif
+template <int D, int VS>
+__device__ __forceinline__ void pv_sched() {
+  __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2 * PV_AHEAD, 0);
+#pragma unroll
+  for (int i = 0; i < 4 * Cfg<D>::DB - PV_AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
+    if (VS > 0) __builtin_amdgcn_sched_group_barrier(SG_VALU, VS, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < PV_AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+    if (VS > 0) __builtin_amdgcn_sched_group_barrier(SG_VALU, VS, 0);
+  }
+}
+
 // O^T += V^T P^T.  V^T fragments by transpose reads: in each 16-lane group (i = lane %
 // 16), lane i addresses 4 dims (4 (i % 4) + 16 ((lane / 16) & 1) + 32 db) of key row
 // (step base + 4 g + i / 4); the read hands lane i those 4 keys at dim (lane % 32) + 32 db.
 // Two reads (rows +0 and +8) give the 8 keys of one 16-key step.
-template <int D>
+template <int D, bool SCHED = true>
 __device__ __forceinline__ void pv_tile(const __bf16 *Vs, const bf16x8_t (&p)[2][2],
                                         f32x16_t (&o)[Cfg<D>::DB]) {
   using C = Cfg<D>;
@@ -514,13 +553,7 @@ __device__ __forceinline__ void pv_tile(const __bf16 *Vs, const bf16x8_t (&p)[2]
                                                          p[kb][cc], o[db], 0, 0, 0);
       }
   // schedule: two MFMAs' operands (four transpose reads) ahead, then two reads per MFMA
-  __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2 * PV_AHEAD, 0);
-#pragma unroll
-  for (int i = 0; i < 4 * C::DB - PV_AHEAD; ++i) {
-    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(SG_MFMA, PV_AHEAD, 0);
+  if constexpr (SCHED) pv_sched<D, 0>();
 }
 
 // ---------------------------------------------------------------------------------------
@@ -719,13 +752,17 @@ __device__ __forceinline__ void pp_rows256(const Ring &r, const qi_tile &tl, int
 
   f32x16_t s[2];
   bf16x8_t p[2][2];
+  float mc = 0.0f;   // c times the row max of the tile in s, taken in the MFMA phase
   auto tile = [&](auto slot, int t) {
     constexpr int T = decltype(slot)::value;   // t & 3
+    // MFMA phase: S of tile t, then O += PV of tile t - 1 with the row max of S taken
+    // meanwhile; the running max is raised after that PV (and before tile t's exp)
     auto mfma = [&]() {
       __builtin_amdgcn_s_setprio(1);
       if (active) {
         if (t < n) qk_tile<D>(QI_RING(r, K, T), qf, s);
         if (t >= 1) pv_tile<D>(QI_RING(r, V, (T + 3) & 3), p, acc);
+        mc = tile_max(s, c);   // stale when t == n: unused
       }
       __builtin_amdgcn_s_setprio(0);
     };
@@ -734,7 +771,8 @@ __device__ __forceinline__ void pp_rows256(const Ring &r, const qi_tile &tl, int
       mfma();
     } else {
       if (active && t >= 1 && t <= n) {
-        softmax_max<D>(s, acc, m_run, l_run, t - 1, tl.kend, c);
+        raise_max<D>(acc, m_run, l_run, mc);
+        if (t * BN > tl.kend) mask_tile(s, t - 1, tl.kend);   // tile t - 1 is PARTIAL
         softmax_exp(s, m_run, c, l_run, p);
       }
       __builtin_amdgcn_s_waitcnt(0);
@@ -747,7 +785,8 @@ __device__ __forceinline__ void pp_rows256(const Ring &r, const qi_tile &tl, int
       mfma();
     } else {
       if (active && t < n) {
-        softmax_max<D>(s, acc, m_run, l_run, t, tl.kend, c);
+        raise_max<D>(acc, m_run, l_run, mc);
+        if ((t + 1) * BN > tl.kend) mask_tile(s, t, tl.kend);   // tile t is PARTIAL
         softmax_exp(s, m_run, c, l_run, p);
       }
       __builtin_amdgcn_s_waitcnt(0);
@@ -812,6 +851,7 @@ __device__ __forceinline__ void pp_rows128(const Ring &r, const qi_tile &tl, int
 
   f32x16_t s[2];
   bf16x8_t p[2][2];
+  float mc = 0.0f;   // c times the row max of the tile in s, taken in the MFMA phase
   auto period = [&](auto slot, int per) {
     constexpr int P = decltype(slot)::value;   // per & 3
     if ((P & 1) == group) {
@@ -819,11 +859,13 @@ __device__ __forceinline__ void pp_rows128(const Ring &r, const qi_tile &tl, int
       if (active) {
         if (per < n) qk_tile<D>(QI_RING(r, K, P), qf, s);
         if (per >= 2) pv_tile<D>(QI_RING(r, V, (P + 2) & 3), p, acc);
+        mc = tile_max(s, c);   // stale when per >= n: unused
       }
       __builtin_amdgcn_s_setprio(0);
     } else {
       if (active && per >= 1 && per <= n) {
-        softmax_max<D>(s, acc, m_run, l_run, per - 1, tl.kend, c);
+        raise_max<D>(acc, m_run, l_run, mc);
+        if (per * BN > tl.kend) mask_tile(s, per - 1, tl.kend);   // tile per - 1 is PARTIAL
         softmax_exp(s, m_run, c, l_run, p);
       }
       __builtin_amdgcn_s_waitcnt(0);   // this group's loads of two periods ago
