@@ -709,10 +709,11 @@ __device__ __forceinline__ __bf16 *q_stage(const Ring &r) {
 
 // Row tiles of more than 128 rows: wavefront w owns rows 32w..32w+31 and every key tile
 // is read by all eight wavefronts (group 0 = waves 0..3, group 1 = waves 4..7).
-//   period 2t:   group 0 MFMA phase t: S = QK^T(K_t) (t < n), O += PV(V_{t-1}) (t >= 1)
-//                group 1 VALU phase:  P = softmax(tile t-1); waits; loads its halves of
-//                                     K_{t+2}, V_{t+1} (t >= 1)
-//   period 2t+1: group 1 MFMA phase t; group 0 VALU phase: P = softmax(tile t); waits;
+//   period 2t:   group 0 MFMA phase t: S = QK^T(K_t) (t < n), O += PV(V_{t-1}) (t >= 1),
+//                                     then the row max of S
+//                group 1 VALU phase:  raise the max, P = exp of tile t-1; waits; loads its
+//                                     halves of K_{t+2} (t >= 1), V_{t+1}
+//   period 2t+1: group 1 MFMA phase t; group 0 VALU phase: the same for tile t; waits;
 //                                     loads its halves of K_{t+3}, V_{t+2}
 // Group g loads half g of each tile's rows.  K_0..K_2 and V_0 are loaded before period 0,
 // together with each wavefront's Q rows, staged in the slots still free (K3, V1..V3);
@@ -811,8 +812,9 @@ __device__ __forceinline__ void pp_rows256(const Ring &r, const qi_tile &tl, int
 
 // Row tiles of at most 128 rows: wavefronts w and w+4 hold the same 32 rows and the two
 // groups split the key tiles (tile t belongs to group t & 1).  Period p = 0 .. n+1:
-//   MFMA group (p & 1):       S = QK^T(K_p) if p < n;  O += PV(V_{p-2}, P) if p >= 2
-//   VALU group ((p + 1) & 1): P = softmax(S of tile p-1) if 1 <= p <= n; waits for its
+//   MFMA group (p & 1):       S = QK^T(K_p) if p < n;  O += PV(V_{p-2}, P) if p >= 2;
+//                             the row max of S
+//   VALU group ((p + 1) & 1): raise the max, P = exp of tile p-1 if 1 <= p <= n; waits for its
 //                             loads of two periods ago; loads K_{p+3}, V_{p+1} (its own
 //                             MFMA phase reads them in period p+3), overwriting K_{p-1}
 //                             and V_{p-3}, last read in period p-1.
