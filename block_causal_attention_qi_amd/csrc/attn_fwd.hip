@@ -493,33 +493,11 @@ __device__ __forceinline__ void softmax_exp_vscaled(const f32x16_t (&s)[2], floa
   l_run = __builtin_fmaf(lt, inv_vs, l_run);
 }
 
-// Instruction order of the PV block: two MFMAs' operands (four transpose reads) ahead, then
-// two reads and VS vector instructions (other work of the same basic block) per MFMA.
-constexpr int SG_VALU = 0x002;
-#ifndef QI_PV_VALU
-#define QI_PV_VALU 2
-#endif
-template <int D, int VS>
-__device__ __forceinline__ void pv_sched() {
-  __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2 * PV_AHEAD, 0);
-#pragma unroll
-  for (int i = 0; i < 4 * Cfg<D>::DB - PV_AHEAD; ++i) {
-    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
-    if (VS > 0) __builtin_amdgcn_sched_group_barrier(SG_VALU, VS, 0);
-  }
-#pragma unroll
-  for (int i = 0; i < PV_AHEAD; ++i) {
-    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-    if (VS > 0) __builtin_amdgcn_sched_group_barrier(SG_VALU, VS, 0);
-  }
-}
-
 // O^T += V^T P^T.  V^T fragments by transpose reads: in each 16-lane group (i = lane %
 // 16), lane i addresses 4 dims (4 (i % 4) + 16 ((lane / 16) & 1) + 32 db) of key row
 // (step base + 4 g + i / 4); the read hands lane i those 4 keys at dim (lane % 32) + 32 db.
 // Two reads (rows +0 and +8) give the 8 keys of one 16-key step.
-template <int D, bool SCHED = true>
+template <int D>
 __device__ __forceinline__ void pv_tile(const __bf16 *Vs, const bf16x8_t (&p)[2][2],
                                         f32x16_t (&o)[Cfg<D>::DB]) {
   using C = Cfg<D>;
@@ -553,7 +531,13 @@ __device__ __forceinline__ void pv_tile(const __bf16 *Vs, const bf16x8_t (&p)[2]
                                                          p[kb][cc], o[db], 0, 0, 0);
       }
   // schedule: two MFMAs' operands (four transpose reads) ahead, then two reads per MFMA
-  if constexpr (SCHED) pv_sched<D, 0>();
+  __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2 * PV_AHEAD, 0);
+#pragma unroll
+  for (int i = 0; i < 4 * C::DB - PV_AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(SG_MFMA, PV_AHEAD, 0);
 }
 
 // ---------------------------------------------------------------------------------------
