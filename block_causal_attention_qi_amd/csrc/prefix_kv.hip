@@ -16,12 +16,12 @@
 //   pass 1  every workgroup takes 64 tokens of one (request, head) and writes the max |x|
 //           of K and of V over them to the workspace (no atomics: max is exact, so the
 //           result does not depend on any order);
-//   pass 2  every workgroup reduces its (request, head)'s partials, derives scale = a/448
-//           and inv = 448/a (correctly rounded float32 divisions; a == 0 gives 1 and 1),
-//           the first workgroup stores the scales, and all quantise their tokens: code =
-//           nearest E4M3FN value to x*inv (float32 product), ties to the even code,
-//           saturating at 448.
-// Every kernel runs one workgroup per (64-token chunk, request, head).
+//   pass 2  one workgroup per (request, head) reduces its partials to the absmax a;
+//   pass 3  every workgroup derives scale = a/448 and inv = 448/a (correctly rounded
+//           float32 divisions; a == 0 gives 1 and 1), the first workgroup of a (request,
+//           head) stores the scales, and all quantise their tokens: code = nearest E4M3FN
+//           value to x*inv (float32 product), ties to the even code, saturating at 448.
+// The copy and passes 1 and 3 run one workgroup per (64-token chunk, request, head).
 #include <hip/hip_runtime.h>
 
 #include "qi_internal.h"
@@ -122,9 +122,28 @@ __global__ __launch_bounds__(NT) void cache_absmax_fp8(const qi_req_dev *__restr
   }
 }
 
-// Pass 2, workgroup (chunk x, request y, head z): reduce the request's partials of head z
-// to the scales, store them (chunk 0), quantise the chunk's tokens of head z.  K8 false
-// (the V-only cache): K is copied as bf16 and its scale stored as 1.
+// Pass 2, workgroup (request x, head y): reduce the request's per-chunk partials of head y
+// to its absmax of K and of V, written over the chunk-0 partials (read by pass 3).
+__global__ __launch_bounds__(NT) void cache_absmax_reduce(const qi_req_dev *__restrict__ reqs,
+                                                          int H, float *__restrict__ partials) {
+  __shared__ float red[NT / 64];
+  const qi_req_dev r = reqs[blockIdx.x];
+  const int h = blockIdx.y;
+  float m[2] = {0.0f, 0.0f};
+  for (int c = threadIdx.x; c < r.n_chunks; c += NT) {
+#pragma unroll
+    for (int w = 0; w < 2; ++w) m[w] = fmaxf(m[w], partials[r.part_idx + (c * 2 + w) * H + h]);
+  }
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    const float a = block_max(m[w], red);   // every read above precedes its barriers
+    if (threadIdx.x == 0) partials[r.part_idx + w * H + h] = a;
+  }
+}
+
+// Pass 3, workgroup (chunk x, request y, head z): turn the request's absmax of head z into
+// the scales, store them (chunk 0), quantise the chunk's tokens of head z.  K8 false (the
+// V-only cache): K is copied as bf16 and its scale stored as 1.
 template <bool K8>
 __global__ __launch_bounds__(NT) void cache_quant_fp8(const qi_req_dev *__restrict__ reqs,
                                                       int H, int D,
@@ -138,8 +157,7 @@ __global__ __launch_bounds__(NT) void cache_quant_fp8(const qi_req_dev *__restri
   float inv[2];
 #pragma unroll
   for (int w = 0; w < 2; ++w) {
-    float a = 0.0f;
-    for (int c = 0; c < r.n_chunks; ++c) a = fmaxf(a, partials[r.part_idx + (c * 2 + w) * H + h]);
+    const float a = partials[r.part_idx + w * H + h];   // reduced by pass 2
     inv[w] = a > 0.0f ? __fdiv_rn(448.0f, a) : 1.0f;
     const float scale = (w == 0 && !K8) ? 1.0f : a > 0.0f ? __fdiv_rn(a, 448.0f) : 1.0f;
     if (blockIdx.x == 0 && threadIdx.x == 0)
@@ -186,6 +204,8 @@ qi_status qi_launch_cache_write(const qi_plan *p, const void *k_pre, const void 
   } else {
     float *part = reinterpret_cast<float *>(ws + p->part_off);
     hipLaunchKernelGGL(cache_absmax_fp8, grid, dim3(NT), 0, s, reqs, p->H, p->D, k, v, part);
+    if (hipGetLastError() != hipSuccess) return QI_ERR_HIP;
+    hipLaunchKernelGGL(cache_absmax_reduce, dim3(p->n_req, p->H), dim3(NT), 0, s, reqs, p->H, part);
     if (hipGetLastError() != hipSuccess) return QI_ERR_HIP;
     auto quant = p->kv == QI_KV_FP8_E4M3 ? cache_quant_fp8<true> : cache_quant_fp8<false>;
     hipLaunchKernelGGL(quant, grid, dim3(NT), 0, s, reqs, p->H, p->D, k, v, (const float *)part, c);
