@@ -10,7 +10,7 @@ Prints ONE JSON line.  `value` is useful attention TFLOP/s (4*D*H*allowed pairs;
 pairs are not counted) on the 1024x1024 text-to-image workload (24 heads x 128, text 256
 + image 4096 tokens); the 2048x2048 edit and the others are reported under "extra".
 
-    python bench.py [--steps K] [--warmup W] [--workload t2i1024] [--extra] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--workload t2i1024] [--kv fp8] [--extra] [--no-cpu]
 """
 from __future__ import annotations
 
@@ -224,6 +224,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--workload", default="t2i1024")
+    ap.add_argument("--kv", choices=["bf16", "fp8", "fp8_v"], default=None,
+                    help="prefix cache type of the main workload (default: the workload's own)")
     ap.add_argument("--extra", action="store_true",
                     help="also time edit4 (cached vs full), wave8 (fp8) and edit10 (ten "
                          "references: cached vs full, and the fp8 / fp8_v caches)")
@@ -248,7 +250,7 @@ def main():
     from block_causal_attention_qi_amd import qi  # noqa: F401  (fails loudly if not built)
 
     main_res = measure(a.workload, a.steps, a.warmup, a.layers, dev, with_full=False,
-                       with_graph=True)
+                       with_graph=True, kv=a.kv)
     log("[bench] %s" % json.dumps(main_res))
     extra = {}
     if not a.no_extra:
@@ -269,7 +271,7 @@ def main():
             for kv in ("bf16", "fp8", "fp8_v"):
                 key = "edit10" if kv == "bf16" else "edit10_" + kv
                 extra[key] = measure("edit10", 2, 1, min(a.layers, 8), dev,
-                                     with_full=(kv == "bf16"), with_build=(kv == "bf16"), kv=kv)
+                                     with_full=(kv == "bf16"), kv=kv)
                 log("[bench] %s" % json.dumps(extra[key]))
 
     traffic = None
@@ -314,6 +316,8 @@ def main():
         "note": "the same %d-layer step captured once in a HIP graph and replayed" % a.layers}
     if not a.no_cpu:
         out["cpu_baseline"] = cpu_baseline(a.workload)
+        if main_res["kv_cache"] != "bf16":
+            out["cpu_baseline"]["sample"] += " (bf16 prefix values, not the %s cache)" % main_res["kv_cache"]
         log("[bench] cpu baseline %s" % json.dumps(out["cpu_baseline"]))
     print(json.dumps(out), flush=True)
 
