@@ -31,15 +31,16 @@
 // access of the kernel is free of bank conflicts on the 64-bank gfx950 LDS (16 lanes per
 // cycle for 16-byte reads, 32 lanes per cycle for 8-byte reads).
 //
-// bf16 sources (full call, prefix call, denoising call on a bf16 cache): a workgroup of
-// 8 wavefronts (two per SIMD) in two groups of four that alternate an MFMA phase and a
-// VALU phase (softmax, tile loads straight from global memory into LDS) between
+// Every call and cache type: a workgroup of 8 wavefronts (two per SIMD) in two groups of
+// four that alternate an MFMA phase and a VALU phase (softmax, tile loads) between
 // workgroup barriers ("ping-pong"), so each SIMD always has one wavefront feeding the
 // matrix core and one feeding the vector ALU.  Row tiles of 256 rows give each wavefront
 // its own 32 rows; row tiles of 128 rows give two wavefronts the same rows, the two
 // groups split the key tiles, and the two partial softmax states are merged through LDS
-// in a fixed order.  The fp8 caches are staged through registers by 4 wavefronts with a
-// plain loop.
+// in a fixed order.  bf16 rows go straight from global memory into LDS; tiles wholly in
+// an E4M3FN cache land there as codes and are converted to bf16 code values by the
+// wavefront that loaded them, one VALU phase later, with the per-head scales folded into
+// the logit scale (K) and into P (V).
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -57,8 +58,7 @@ typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int BN = QI_KERNEL_BN;
-constexpr int NT = 512;                 // ping-pong kernel: 8 wavefronts
-constexpr int NT_STAGED = 256;          // register-staged kernel: 4 wavefronts
+constexpr int NT = 512;                 // 8 wavefronts
 constexpr float TAU = 8.0f;   // lazy-rescale threshold, log2 units
 
 // instruction classes of __builtin_amdgcn_sched_group_barrier
@@ -82,13 +82,11 @@ __host__ __device__ constexpr bool coded(int src, int which) {
 template <int D>
 struct Cfg {
   static constexpr int CH = D / 8;           // 16-byte chunks per K/V row
-  static constexpr int ROWS = NT_STAGED / CH;   // rows staged per pass (register staging)
-  static constexpr int PASS = BN / ROWS;        // passes per tile
   static constexpr int QS = D / 16;          // MFMA k-steps over the head dim
   static constexpr int DB = D / 32;          // 32-wide blocks of the output
   static constexpr int IPW = D / 32;         // 1 KiB direct V loads per wavefront per tile
   static constexpr int RPK = 512 / D;        // V rows per 1 KiB
-  static_assert(PASS * ROWS == BN && IPW * RPK * 4 == BN, "tile shape");
+  static_assert(IPW * RPK * 4 == BN, "tile shape");
   // K tile: rows of 2D bytes; logical 16-byte chunk c of row r sits at chunk c ^ ks(r), so
   // the 16 consecutive rows one 16-byte MFMA-operand read touches (one chunk each) fall in
   // 16 distinct bank groups.
@@ -168,7 +166,7 @@ __device__ __forceinline__ int tile_kind(int kt, const TileArgs &a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Direct global -> LDS tile loads (bf16 sources).  Every load instruction fills 1 KiB of
+// Direct global -> LDS tile loads (bf16 rows).  Every load instruction fills 1 KiB of
 // LDS, lane l the 16 bytes at offset 16 l, so the layout is set on the global side: each
 // lane fetches the key row and chunk that belongs at its LDS slot.
 //   K and V: KiB kib of a tile holds rows kib * RPK + l / CH; physical chunk p of row r is
@@ -255,96 +253,147 @@ struct Direct {
 };
 
 // ---------------------------------------------------------------------------------------
-// Register-staged tile loads (fp8 caches): lane t stages chunk t % CH of rows
-// t / CH + i * ROWS (i < PASS) of both tiles.  Tiles wholly from the cache hold the code
-// values (exact in bf16) and the kernel applies the scales: K's folds into the logit
-// scale, V's into P.  Tiles mixing cached and live rows hold code * scale rounded to bf16.
-template <int D, int SRC>
-struct Stage {
+// E4M3FN cache tiles in the ping-pong kernel.  A key tile lying wholly in an E4M3FN cache
+// tensor is loaded as codes (1 byte per element, rows contiguous in the head-major cache)
+// straight into a landing buffer, and converted to bf16 code values (exact) in the ring
+// slot by the same wavefront in its next VALU phase, after its wait.  Each group lands its
+// rows (HALF: its 32-row half of the tile; else the whole tile) in its own landing region
+// of BN x D bytes.  A wavefront converts exactly the bytes it loaded, so no barrier is
+// needed between landing and conversion.  Tiles that mix cached and live keys, or reach
+// past kend, take a synchronous per-lane path instead (sync_tile).
+template <int D, bool HALF>
+struct Coded {
+  static constexpr int ROWS = HALF ? 32 : 64;            // rows one group loads per tile
+  static constexpr int NIC = ROWS * D / 1024;            // 1 KiB code loads per group
+  static constexpr int PER = (NIC + 3) / 4;              // per wavefront, at most
+  static constexpr int REGION = BN * D;                  // landing bytes per group
+  int w;   // wavefront index in the group (uniform)
+
+  __device__ __forceinline__ void init() { w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 3; }
+
+  // codes of tile kt (the group's rows) from cache tensor `coff` into the group's region
+  __device__ __forceinline__ void issue(int kt, const TileArgs &a, int64_t coff, uint8_t *land,
+                                        int hf) const {
+    const int k0 = kt * BN + (HALF ? 32 * hf : 0);
+    const char *base = reinterpret_cast<const char *>(a.cache + coff) + (int64_t)(a.h * a.lp + k0) * D;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int ins = w + 4 * u;
+      if (ins < NIC)
+        __builtin_amdgcn_global_load_lds(base + ins * 1024 + lane * 16,
+                                         (lds_void_t *)(land + hf * REGION + ins * 1024), 16, 0, 0);
+    }
+  }
+
+  // the codes this wavefront landed for tile rows of half hf -> bf16 code values in `tile`
+  template <bool IS_K>
+  __device__ __forceinline__ void convert(const uint8_t *land, __bf16 *tile, int hf) const {
+    using C = Cfg<D>;
+    const int lane = threadIdx.x & 63;
+    char *tb = reinterpret_cast<char *>(tile);
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int ins = w + 4 * u;
+      if (ins < NIC) {
+        const int byte = ins * 1024 + lane * 16;   // 16 codes: row byte / D, chunks c0, c0 + 1
+        const uint4 cd = *reinterpret_cast<const uint4 *>(land + hf * REGION + byte);
+        const int r = (HALF ? 32 * hf : 0) + byte / D, c0 = (byte % D) / 8;
+        *reinterpret_cast<uint4 *>(tb + (IS_K ? C::koff(r, c0) : C::voff(r, c0))) = codes8(cd.x, cd.y);
+        *reinterpret_cast<uint4 *>(tb + (IS_K ? C::koff(r, c0 + 1) : C::voff(r, c0 + 1))) =
+            codes8(cd.z, cd.w);
+      }
+    }
+  }
+};
+
+// Synchronous per-lane load of one tile of a coded cache tensor (the rows of half hf, or
+// the whole tile), written to the ring slot in the layout the direct loads produce: cached
+// rows as code values (tile wholly cached) or code * scale rounded to bf16 (mixed tile),
+// live rows as they are, rows past kend as key kend - 1.  Waits for its loads.
+template <int D, int SRC, bool HALF, bool IS_K>
+__device__ __forceinline__ void sync_tile(int kt, const TileArgs &a, const __bf16 *live,
+                                          int64_t coff, __bf16 *tile, int hf) {
   using C = Cfg<D>;
-  uint4 kr[C::PASS];
-  uint4 vr[C::PASS];
-  int row0, chunk;
-  int live_off[C::PASS];
-  int cache_off[C::PASS];
-
-  __device__ __forceinline__ void init(const TileArgs &a) {
-    row0 = threadIdx.x / C::CH;      // NT_STAGED lanes
-    chunk = threadIdx.x % C::CH;
+  constexpr int NI = HALF ? 2 * C::IPW : 4 * C::IPW;   // 1 KiB stores per tensor
+  constexpr int U = NI / 4;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 3;
+  const int l = threadIdx.x & 63;
+  const int k0 = kt * BN + (HALF ? 32 * hf : 0);
+  const bool whole = tile_kind<SRC>(kt, a) == CACHED;
+  const float scale = IS_K ? a.k_scale : a.v_scale;
+  char *tb = reinterpret_cast<char *>(tile);
 #pragma unroll
-    for (int i = 0; i < C::PASS; ++i) {
-      const int r = row0 + i * C::ROWS;
-      live_off[i] = r * a.H * D + chunk * 8;
-      cache_off[i] = r * D + chunk * 8;
-    }
-  }
-
-  // 8 elements of a cached row: 8 codes in the low half, or 8 bf16
-  template <bool CODED>
-  __device__ __forceinline__ static uint4 cached8(const uint8_t *row_base, int64_t off) {
-    if (CODED) {
-      const uint2 raw = *reinterpret_cast<const uint2 *>(row_base + off);
-      return make_uint4(raw.x, raw.y, 0, 0);
-    }
-    return *reinterpret_cast<const uint4 *>(row_base + 2 * off);
-  }
-
-  template <bool CODED>
-  __device__ __forceinline__ uint4 fetch_row(const __bf16 *live, int64_t coff, int key,
-                                             const TileArgs &a) const {
-    if (key >= a.kend) return make_uint4(0, 0, 0, 0);
-    if (SRC != SRC_ONE && key < a.lp)
-      return cached8<CODED>(a.cache + coff, (int64_t)(a.h * a.lp + key) * D + chunk * 8);
-    const __bf16 *p = live + ((int64_t)(a.kv_tok + key - a.lp) * a.H + a.h) * D + chunk * 8;
-    return *reinterpret_cast<const uint4 *>(p);
-  }
-
-  __device__ __forceinline__ void load(int kt, const TileArgs &a) {
-    const int k0 = kt * BN;
-    const int kd = tile_kind<SRC>(kt, a);
-    if (kd == LIVE) {
-      const int64_t base = ((int64_t)(a.kv_tok + k0 - a.lp) * a.H + a.h) * D;
-      const __bf16 *kb = a.k + base, *vb = a.v + base;
-#pragma unroll
-      for (int i = 0; i < C::PASS; ++i) {
-        kr[i] = *reinterpret_cast<const uint4 *>(kb + live_off[i]);
-        vr[i] = *reinterpret_cast<const uint4 *>(vb + live_off[i]);
-      }
-    } else if (kd == CACHED) {
-      const int64_t e0 = (int64_t)(a.h * a.lp + k0) * D;
-      const uint8_t *kb = a.cache + a.k_off + e0 * (coded(SRC, 0) ? 1 : 2);
-      const uint8_t *vb = a.cache + a.v_off + e0 * (coded(SRC, 1) ? 1 : 2);
-#pragma unroll
-      for (int i = 0; i < C::PASS; ++i) {
-        kr[i] = cached8<coded(SRC, 0)>(kb, cache_off[i]);
-        vr[i] = cached8<coded(SRC, 1)>(vb, cache_off[i]);
-      }
+  for (int u = 0; u < U; ++u) {
+    const int ins = U * w + u;
+    const int r = ins * C::RPK + l / C::CH;
+    const int ch = (l % C::CH) ^ (IS_K ? C::ks(r) : (C::vq(r) << 2));
+    const int key = min(k0 + r, a.kend - 1);
+    uint4 val;
+    if (key < a.lp) {
+      const uint2 raw = *reinterpret_cast<const uint2 *>(a.cache + coff + (int64_t)(a.h * a.lp + key) * D + ch * 8);
+      val = whole ? codes8(raw.x, raw.y) : dequant8(raw.x, raw.y, scale);
     } else {
-#pragma unroll
-      for (int i = 0; i < C::PASS; ++i) {
-        const int key = k0 + row0 + i * C::ROWS;
-        kr[i] = fetch_row<coded(SRC, 0)>(a.k, a.k_off, key, a);
-        vr[i] = fetch_row<coded(SRC, 1)>(a.v, a.v_off, key, a);
-      }
+      val = *reinterpret_cast<const uint4 *>(live + ((int64_t)(a.kv_tok + key - a.lp) * a.H + a.h) * D + ch * 8);
     }
+    *reinterpret_cast<uint4 *>(tb + (HALF ? hf * (NI * 1024) : 0) + ins * 1024 + l * 16) = val;
   }
+}
 
-  __device__ __forceinline__ void store(int kt, const TileArgs &a, __bf16 *Ks, __bf16 *Vs) {
-    const int kd = tile_kind<SRC>(kt, a);
-#pragma unroll
-    for (int i = 0; i < C::PASS; ++i) {
-      const int r = row0 + i * C::ROWS;
-      uint4 kv = kr[i], vv = vr[i];
-      if (kd == CACHED) {   // code values; the scales are applied in the softmax
-        if (coded(SRC, 0)) kv = codes8(kv.x, kv.y);
-        if (coded(SRC, 1)) vv = codes8(vv.x, vv.y);
-      } else if (kd == MIXED && kt * BN + r < a.lp && kt * BN + r < a.kend) {
-        if (coded(SRC, 0)) kv = dequant8(kv.x, kv.y, a.k_scale);
-        if (coded(SRC, 1)) vv = dequant8(vv.x, vv.y, a.v_scale);
+// Tile loads of the ping-pong kernel for any source: direct loads for bf16 rows, landing
+// and conversion for tiles wholly in an E4M3FN cache tensor, the synchronous path for
+// mixed coded tiles.  Scales of coded tiles are folded in: K's into the logit scale (ck),
+// V's into P (vsc).
+template <int D, int SRC, bool HALF>
+struct Loader {
+  static constexpr bool CK = coded(SRC, 0), CV = coded(SRC, 1);
+  Direct<D, SRC, HALF> dm;
+  Coded<D, HALF> cm;
+  uint8_t *lk, *lv;   // landing buffers of the coded tensors
+
+  __device__ __forceinline__ void init(const TileArgs &a, uint8_t *lk_, uint8_t *lv_) {
+    dm.init(a);
+    cm.init();
+    lk = lk_;
+    lv = lv_;
+  }
+  // before the loop: every tile straight into its ring slot
+  template <bool IS_K>
+  __device__ __forceinline__ void pro(int m, const TileArgs &a, __bf16 *slot, int hf = 0) {
+    if constexpr (IS_K ? CK : CV)
+      sync_tile<D, SRC, HALF, IS_K>(m, a, IS_K ? a.k : a.v, IS_K ? a.k_off : a.v_off, slot, hf);
+    else
+      dm.template issue<IS_K>(m, a, IS_K ? a.k : a.v, IS_K ? a.k_off : a.v_off, slot, hf);
+  }
+  // in the loop: cached coded tiles land and are converted two periods later
+  template <bool IS_K>
+  __device__ __forceinline__ void issue(int m, const TileArgs &a, __bf16 *slot, int hf = 0) {
+    if constexpr (IS_K ? CK : CV) {
+      const int kd = tile_kind<SRC>(m, a);
+      if (kd == CACHED) {
+        cm.issue(m, a, IS_K ? a.k_off : a.v_off, IS_K ? lk : lv, hf);
+        return;
       }
-      *reinterpret_cast<uint4 *>(reinterpret_cast<char *>(Ks) + C::koff(r, chunk)) = kv;
-      *reinterpret_cast<uint4 *>(reinterpret_cast<char *>(Vs) + C::voff(r, chunk)) = vv;
+      if (kd == MIXED) {
+        sync_tile<D, SRC, HALF, IS_K>(m, a, IS_K ? a.k : a.v, IS_K ? a.k_off : a.v_off, slot, hf);
+        return;
+      }
     }
+    dm.template issue<IS_K>(m, a, IS_K ? a.k : a.v, IS_K ? a.k_off : a.v_off, slot, hf);
+  }
+  // convert tile m if it was landed (the caller knows it was issued two periods ago)
+  template <bool IS_K>
+  __device__ __forceinline__ void convert(int m, const TileArgs &a, __bf16 *slot, int hf = 0) const {
+    if constexpr (IS_K ? CK : CV)
+      if (tile_kind<SRC>(m, a) == CACHED) cm.template convert<IS_K>(IS_K ? lk : lv, slot, hf);
+  }
+  __device__ __forceinline__ float ck(int m, const TileArgs &a, float c) const {
+    if constexpr (CK) return tile_kind<SRC>(m, a) == CACHED ? c * a.k_scale : c;
+    return c;
+  }
+  __device__ __forceinline__ bool vsc(int m, const TileArgs &a) const {
+    if constexpr (CV) return tile_kind<SRC>(m, a) == CACHED;
+    return false;
   }
 };
 
@@ -435,16 +484,6 @@ __device__ __forceinline__ void raise_max(f32x16_t (&o)[Cfg<D>::DB], float &m_ru
   }
 }
 
-// Mask the tail tile, take the row max, raise the running max when it is exceeded by
-// more than TAU (rescaling O and l exactly).
-template <int D>
-__device__ __forceinline__ void softmax_max(f32x16_t (&s)[2], f32x16_t (&o)[Cfg<D>::DB],
-                                            float &m_run, float &l_run, int kt, int kend,
-                                            float c) {
-  if ((kt + 1) * BN > kend) mask_tile(s, kt, kend);   // the PARTIAL tile
-  raise_max<D>(o, m_run, l_run, tile_max(s, c));
-}
-
 // P = 2^(s c - m) in bf16, in the MFMA B-operand order: step (kb, cc) holds keys
 // 32kb + 16cc + {4g..4g+3, 8+4g..8+4g+3}, i.e. this lane's score registers 8cc..8cc+7.
 // The row sum accumulates the fp32 values before rounding (plain adds: they overlap the
@@ -491,6 +530,18 @@ __device__ __forceinline__ void softmax_exp_vscaled(const f32x16_t (&s)[2], floa
       p[kb][cc] = __builtin_bit_cast(bf16x8_t, u);
     }
   l_run = __builtin_fmaf(lt, inv_vs, l_run);
+}
+
+// The exponential step of a tile: bf16 sources as softmax_exp; E4M3FN caches with the
+// folded scales (ck: logit scale of the tile, vs: its V rows are code values).
+template <bool FP8>
+__device__ __forceinline__ void tile_exp(const f32x16_t (&s)[2], float m_run, float ck, bool vs,
+                                         float log2_vs, float inv_vs, float &l_run,
+                                         bf16x8_t (&p)[2][2]) {
+  if constexpr (FP8)
+    softmax_exp_vscaled(s, m_run, ck, vs ? log2_vs : 0.0f, vs ? inv_vs : 1.0f, l_run, p);
+  else
+    softmax_exp(s, m_run, ck, l_run, p);
 }
 
 // O^T += V^T P^T.  V^T fragments by transpose reads: in each 16-lane group (i = lane %
@@ -575,27 +626,6 @@ __device__ __forceinline__ void read_q_lds(const __bf16 *stage, bf16x8_t (&qf)[C
     qf[st] = *reinterpret_cast<const bf16x8_t *>(sb + C::koff(lane & 31, 2 * st + (lane >> 5)));
 }
 
-// O straight from the accumulators: lane (j, g) writes 8 bytes of row j per instruction.
-template <int D>
-__device__ __forceinline__ void store_o(__bf16 *o, const qi_tile &tl, int H, int h, int row,
-                                        const f32x16_t (&acc)[Cfg<D>::DB], float l_run) {
-  const int lane = threadIdx.x & 63;
-  const int g = lane >> 5;
-  const float inv = 1.0f / pair_sum(l_run);
-  if (row >= tl.nrows) return;
-  __bf16 *op = o + ((int64_t)(tl.q_tok + row) * H + h) * D;
-#pragma unroll
-  for (int db = 0; db < Cfg<D>::DB; ++db)
-#pragma unroll
-    for (int aa = 0; aa < 4; ++aa) {
-      const int dim = db * 32 + 8 * aa + 4 * g;
-      uint2 u;
-      u.x = pack_bf16(acc[db][4 * aa] * inv, acc[db][4 * aa + 1] * inv);
-      u.y = pack_bf16(acc[db][4 * aa + 2] * inv, acc[db][4 * aa + 3] * inv);
-      *reinterpret_cast<uint2 *>(op + dim) = u;
-    }
-}
-
 // O through LDS: the wavefront normalises its 32 rows (O / l, rounded to bf16), writes
 // them into `stage` (32 rows of 2D bytes, chunks placed as in a K tile, so both the
 // 8-byte writes and the 16-byte reads are free of bank conflicts) and reads them back row
@@ -655,18 +685,22 @@ __device__ __forceinline__ TileArgs make_args(const qi_tile &tl, int H, int h, c
 }
 
 // ---------------------------------------------------------------------------------------
-// Ping-pong kernel (bf16 sources).  Eight wavefronts in two groups of four alternate an
+// Ping-pong kernel.  Eight wavefronts in two groups of four alternate an
 // MFMA phase and a VALU phase between workgroup barriers ("periods").  K and V tiles live
 // in a ring of four separate LDS arrays per tensor (slot = tile & 3), so that the compiler
 // can tell each direct-load target from every buffer being read and never stalls a read
 // on an unrelated load; the loops are unrolled by four so every slot index is constant.
 // Loads are issued at the end of a group's VALU phase, after that group waited for the
-// loads it issued in its previous VALU phase; the next barrier publishes them.
+// loads it issued in its previous VALU phase (and converted the code tiles among them);
+// the next barrier publishes them.  A code tile reaches its ring slot two periods after
+// its load was issued, as early as a direct load is waited for, so the schedule of first
+// reads is the same for both.
 
 template <int P> struct Slot { static constexpr int value = P; };
 
 struct Ring {
   __bf16 *K0, *K1, *K2, *K3, *V0, *V1, *V2, *V3;
+  uint8_t *LK, *LV;   // landing buffers of E4M3FN code tiles (null when unused)
 };
 #define QI_RING(r, arr, i) \
   ((i) == 0 ? (r).arr##0 : (i) == 1 ? (r).arr##1 : (i) == 2 ? (r).arr##2 : (r).arr##3)
@@ -715,14 +749,17 @@ __device__ __forceinline__ void pp_rows256(const Ring &r, const qi_tile &tl, int
   const bool active = wave * 32 < tl.nrows;   // the wavefront's rows exist
 
   const int n = (tl.kend + BN - 1) / BN;
-  Direct<D, SRC, true> dm;
-  dm.init(a);
+  constexpr bool FP8 = SRC == SRC_CACHE_FP8 || SRC == SRC_CACHE_FP8V;
+  Loader<D, SRC, true> ld;
+  ld.init(a, r.LK, r.LV);
   __bf16 *const qst = q_stage<D>(r);
   issue_q_lds<D>(q, tl, H, h, wave * 32, qst);
-  dm.template issue<true>(0, a, a.k, a.k_off, r.K0, group);
-  if (n > 1) dm.template issue<true>(1, a, a.k, a.k_off, r.K1, group);
-  if (n > 2) dm.template issue<true>(2, a, a.k, a.k_off, r.K2, group);
-  dm.template issue<false>(0, a, a.v, a.v_off, r.V0, group);
+  ld.template pro<true>(0, a, r.K0, group);
+  if (n > 1) ld.template pro<true>(1, a, r.K1, group);
+  if (n > 2) ld.template pro<true>(2, a, r.K2, group);
+  ld.template pro<false>(0, a, r.V0, group);
+  const float log2_vs = FP8 ? __builtin_log2f(a.v_scale) : 0.0f;
+  const float inv_vs = FP8 ? 1.0f / a.v_scale : 1.0f;
   f32x16_t acc[C::DB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
@@ -747,7 +784,7 @@ __device__ __forceinline__ void pp_rows256(const Ring &r, const qi_tile &tl, int
       if (active) {
         if (t < n) qk_tile<D>(QI_RING(r, K, T), qf, s);
         if (t >= 1) pv_tile<D>(QI_RING(r, V, (T + 3) & 3), p, acc);
-        mc = tile_max(s, c);   // stale when t == n: unused
+        mc = tile_max(s, ld.ck(t, a, c));   // stale when t == n: unused
       }
       __builtin_amdgcn_s_setprio(0);
     };
@@ -758,11 +795,15 @@ __device__ __forceinline__ void pp_rows256(const Ring &r, const qi_tile &tl, int
       if (active && t >= 1 && t <= n) {
         raise_max<D>(acc, m_run, l_run, mc);
         if (t * BN > tl.kend) mask_tile(s, t - 1, tl.kend);   // tile t - 1 is PARTIAL
-        softmax_exp(s, m_run, c, l_run, p);
+        tile_exp<FP8>(s, m_run, ld.ck(t - 1, a, c), ld.vsc(t - 1, a), log2_vs, inv_vs, l_run, p);
       }
       __builtin_amdgcn_s_waitcnt(0);
-      if (t >= 1 && t + 2 < n) dm.template issue<true>(t + 2, a, a.k, a.k_off, QI_RING(r, K, (T + 2) & 3), 1);
-      if (t + 1 < n) dm.template issue<false>(t + 1, a, a.v, a.v_off, QI_RING(r, V, (T + 1) & 3), 1);
+      // coded tiles this group landed two periods ago: K_{t+1}, V_t
+      if (t >= 2 && t + 1 < n) ld.template convert<true>(t + 1, a, QI_RING(r, K, (T + 1) & 3), 1);
+      if (t >= 1 && t < n) ld.template convert<false>(t, a, QI_RING(r, V, T), 1);
+      if (t >= 1 && t + 2 < n) ld.template issue<true>(t + 2, a, QI_RING(r, K, (T + 2) & 3), 1);
+      if (t + 1 < n) ld.template issue<false>(t + 1, a, QI_RING(r, V, (T + 1) & 3), 1);
+      if (FP8) wait_lds();   // converted tiles are written before the barrier
     }
     bar();
     // period 2t+1
@@ -772,12 +813,17 @@ __device__ __forceinline__ void pp_rows256(const Ring &r, const qi_tile &tl, int
       if (active && t < n) {
         raise_max<D>(acc, m_run, l_run, mc);
         if ((t + 1) * BN > tl.kend) mask_tile(s, t, tl.kend);   // tile t is PARTIAL
-        softmax_exp(s, m_run, c, l_run, p);
+        tile_exp<FP8>(s, m_run, ld.ck(t, a, c), ld.vsc(t, a), log2_vs, inv_vs, l_run, p);
       }
       __builtin_amdgcn_s_waitcnt(0);
-      if (t + 3 < n) dm.template issue<true>(t + 3, a, a.k, a.k_off, QI_RING(r, K, (T + 3) & 3), 0);
-      if (t + 2 < n) dm.template issue<false>(t + 2, a, a.v, a.v_off, QI_RING(r, V, (T + 2) & 3), 0);
-      if (T == 0 && t == 0 && n > 1) dm.template issue<false>(1, a, a.v, a.v_off, r.V1, 0);
+      // coded tiles this group landed two periods ago: K_{t+2}, V_{t+1}
+      if (t >= 1 && t + 2 < n) ld.template convert<true>(t + 2, a, QI_RING(r, K, (T + 2) & 3), 0);
+      if (t >= 1 && t + 1 < n) ld.template convert<false>(t + 1, a, QI_RING(r, V, (T + 1) & 3), 0);
+      if (t + 3 < n) ld.template issue<true>(t + 3, a, QI_RING(r, K, (T + 3) & 3), 0);
+      if (t + 2 < n) ld.template issue<false>(t + 2, a, QI_RING(r, V, (T + 2) & 3), 0);
+      // V_1's half 0 shares this period with V_2's, so it skips the landing buffer
+      if (T == 0 && t == 0 && n > 1) ld.template pro<false>(1, a, r.V1, 0);
+      if (FP8) wait_lds();   // converted tiles are written before the barrier
     }
     bar();
   };
@@ -815,14 +861,17 @@ __device__ __forceinline__ void pp_rows128(const Ring &r, const qi_tile &tl, int
   const bool active = (wave & 3) * 32 < tl.nrows;   // the wavefront's rows exist
 
   const int n = (tl.kend + BN - 1) / BN;
-  Direct<D, SRC, false> dm;
-  dm.init(a);
+  constexpr bool FP8 = SRC == SRC_CACHE_FP8 || SRC == SRC_CACHE_FP8V;
+  Loader<D, SRC, false> ld;   // whole tiles; coded ones land in the group's region
+  ld.init(a, r.LK, r.LV);
   __bf16 *const qst = q_stage<D>(r);   // both groups load their copy of the rows
   issue_q_lds<D>(q, tl, H, h, (wave & 3) * 32, qst);
-  if (group == 0) dm.template issue<true>(0, a, a.k, a.k_off, r.K0);
-  if (group == 1 && n > 1) dm.template issue<true>(1, a, a.k, a.k_off, r.K1);
-  if (group == 0 && n > 2) dm.template issue<true>(2, a, a.k, a.k_off, r.K2);
-  if (group == 1) dm.template issue<false>(0, a, a.v, a.v_off, r.V0);
+  if (group == 0) ld.template pro<true>(0, a, r.K0);
+  if (group == 1 && n > 1) ld.template pro<true>(1, a, r.K1);
+  if (group == 0 && n > 2) ld.template pro<true>(2, a, r.K2);
+  if (group == 1) ld.template pro<false>(0, a, r.V0);
+  const float log2_vs = FP8 ? __builtin_log2f(a.v_scale) : 0.0f;
+  const float inv_vs = FP8 ? 1.0f / a.v_scale : 1.0f;
   f32x16_t acc[C::DB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
@@ -845,18 +894,22 @@ __device__ __forceinline__ void pp_rows128(const Ring &r, const qi_tile &tl, int
       if (active) {
         if (per < n) qk_tile<D>(QI_RING(r, K, P), qf, s);
         if (per >= 2) pv_tile<D>(QI_RING(r, V, (P + 2) & 3), p, acc);
-        mc = tile_max(s, c);   // stale when per >= n: unused
+        mc = tile_max(s, ld.ck(per, a, c));   // stale when per >= n: unused
       }
       __builtin_amdgcn_s_setprio(0);
     } else {
       if (active && per >= 1 && per <= n) {
         raise_max<D>(acc, m_run, l_run, mc);
         if (per * BN > tl.kend) mask_tile(s, per - 1, tl.kend);   // tile per - 1 is PARTIAL
-        softmax_exp(s, m_run, c, l_run, p);
+        tile_exp<FP8>(s, m_run, ld.ck(per - 1, a, c), ld.vsc(per - 1, a), log2_vs, inv_vs, l_run, p);
       }
       __builtin_amdgcn_s_waitcnt(0);   // this group's loads of two periods ago
-      if (per + 3 < n) dm.template issue<true>(per + 3, a, a.k, a.k_off, QI_RING(r, K, (P + 3) & 3));
-      if (per + 1 < n) dm.template issue<false>(per + 1, a, a.v, a.v_off, QI_RING(r, V, (P + 1) & 3));
+      // coded tiles this group landed two periods ago: K_{per+1}, V_{per-1}
+      if (per >= 2 && per + 1 < n) ld.template convert<true>(per + 1, a, QI_RING(r, K, (P + 1) & 3), group);
+      if (per >= 2 && per - 1 < n) ld.template convert<false>(per - 1, a, QI_RING(r, V, (P + 3) & 3), group);
+      if (per + 3 < n) ld.template issue<true>(per + 3, a, QI_RING(r, K, (P + 3) & 3), group);
+      if (per + 1 < n) ld.template issue<false>(per + 1, a, QI_RING(r, V, (P + 1) & 3), group);
+      if (FP8) wait_lds();   // converted tiles are written before the barrier
     }
     bar();
   };
@@ -904,12 +957,22 @@ __global__ __launch_bounds__(NT, 1) void attn_pp_kernel(
   using C = Cfg<D>;
   __shared__ __attribute__((aligned(1024))) __bf16 K0[C::KTILE], K1[C::KTILE], K2[C::KTILE], K3[C::KTILE];
   __shared__ __attribute__((aligned(1024))) __bf16 V0[C::VTILE], V1[C::VTILE], V2[C::VTILE], V3[C::VTILE];
+  // landing buffers of E4M3FN code tiles, one BN x D region per group (coded caches only)
+  uint8_t *lk = nullptr, *lv = nullptr;
+  if constexpr (coded(SRC, 0)) {
+    __shared__ __attribute__((aligned(1024))) uint8_t LK[2 * BN * D];
+    lk = LK;
+  }
+  if constexpr (coded(SRC, 1)) {
+    __shared__ __attribute__((aligned(1024))) uint8_t LV[2 * BN * D];
+    lv = LV;
+  }
   const int item = sched[blockIdx.x];
   if (item < 0) return;   // schedule padding
   const qi_tile tl = tiles[item / H];
   const int h = item % H;
-  const TileArgs a = make_args(tl, H, h, k, v, cache, false);
-  const Ring r{K0, K1, K2, K3, V0, V1, V2, V3};
+  const TileArgs a = make_args(tl, H, h, k, v, cache, SRC == SRC_CACHE_FP8 || SRC == SRC_CACHE_FP8V);
+  const Ring r{K0, K1, K2, K3, V0, V1, V2, V3, lk, lv};
   if (tl.nrows > 128)
     pp_rows256<D, SRC>(r, tl, H, h, a, q, o, c);
   else
@@ -917,80 +980,13 @@ __global__ __launch_bounds__(NT, 1) void attn_pp_kernel(
 }
 #undef QI_RING
 
-// ---------------------------------------------------------------------------------------
-// Register-staged kernel (fp8 cache): plain double-buffered loop.
-template <int D, int SRC>
-__global__ __launch_bounds__(NT_STAGED, 2) void attn_staged_kernel(
-    const int32_t *__restrict__ sched, const qi_tile *__restrict__ tiles, int H,
-    const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
-    __bf16 *__restrict__ o, const uint8_t *__restrict__ cache, float c) {
-  using C = Cfg<D>;
-  __shared__ __attribute__((aligned(1024))) __bf16 lds[2][C::KTILE + C::VTILE];
-
-  const int item = sched[blockIdx.x];
-  if (item < 0) return;
-  const qi_tile tl = tiles[item / H];
-  const int h = item % H;
-  const TileArgs a = make_args(tl, H, h, k, v, cache, SRC == SRC_CACHE_FP8 || SRC == SRC_CACHE_FP8V);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const bool active = wave * 32 < tl.nrows;
-
-  // Q rows staged in buffer 1 (8 KiB per wavefront), free until tile 1 is stored
-  __bf16 *const qst = lds[1] + wave * 32 * D;
-  issue_q_lds<D>(q, tl, H, h, wave * 32, qst);
-  f32x16_t acc[C::DB];
-#pragma unroll
-  for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
-  float m_run = -INFINITY, l_run = 0.0f;
-
-  const int n = (tl.kend + BN - 1) / BN;
-  const float log2_vs = __builtin_log2f(a.v_scale), inv_vs = 1.0f / a.v_scale;
-  Stage<D, SRC> st;
-  st.init(a);
-  st.load(0, a);
-  st.store(0, a, lds[0], lds[0] + C::KTILE);
-  __builtin_amdgcn_s_waitcnt(0);
-  bf16x8_t qf[C::QS];
-  read_q_lds<D>(qst, qf);
-  if (n > 1) st.load(1, a);
-  __syncthreads();
-  for (int j = 0; j < n; ++j) {
-    const int cur = j & 1;
-    if (active) {
-      f32x16_t s[2];
-      bf16x8_t p[2][2];
-      qk_tile<D>(lds[cur], qf, s);
-      // tiles wholly from the cache hold code values: fold the scales in
-      const bool cached = tile_kind<SRC>(j, a) == CACHED;
-      const float ck = cached && coded(SRC, 0) ? c * a.k_scale : c;
-      const bool vs = cached && coded(SRC, 1);
-      softmax_max<D>(s, acc, m_run, l_run, j, tl.kend, ck);
-      softmax_exp_vscaled(s, m_run, ck, vs ? log2_vs : 0.0f, vs ? inv_vs : 1.0f, l_run, p);
-      pv_tile<D>(lds[cur] + C::KTILE, p, acc);
-    }
-    if (j + 1 < n) st.store(j + 1, a, lds[cur ^ 1], lds[cur ^ 1] + C::KTILE);
-    if (j + 2 < n) st.load(j + 2, a);
-    __syncthreads();
-  }
-  // (two workgroups share a CU here, so the other one computes while this one stores:
-  // staging O through LDS measured no faster, and costs registers)
-  if (active) store_o<D>(o, tl, H, h, wave * 32 + (threadIdx.x & 31), acc, l_run);
-}
-
 template <int D, int SRC>
 qi_status launch(const qi_plan *p, int call, const void *q, const void *k, const void *v,
                  void *o, const void *cache, hipStream_t s) {
   const uint8_t *ws = static_cast<const uint8_t *>(p->d_ws);
   const float c = (float)(1.4426950408889634 / std::sqrt((double)D));   // log2(e)/sqrt(D)
-  constexpr bool staged = SRC == SRC_CACHE_FP8 || SRC == SRC_CACHE_FP8V;
-  decltype(&attn_pp_kernel<D, SRC_ONE>) kern;
-  if constexpr (staged)
-    kern = attn_staged_kernel<D, SRC>;
-  else
-    kern = attn_pp_kernel<D, SRC>;
-  const int nt = staged ? NT_STAGED : NT;
+  const auto kern = attn_pp_kernel<D, SRC>;
+  const int nt = NT;
   hipLaunchKernelGGL(kern, dim3(p->sched_len[call]), dim3(nt), 0, s,
                      reinterpret_cast<const int32_t *>(ws + p->sched_off[call]),
                      reinterpret_cast<const qi_tile *>(ws + p->tiles_off[call]), p->H,

@@ -301,18 +301,16 @@ qi_status qi_plan_create(const qi_wave_desc *d, qi_plan **out) {
   // so every row runs the same kernel path over the same key tiles in every call and the
   // results agree bit for bit (reuse is exact).
   for (int c : {QI_CALL_PREFIX, QI_CALL_DENOISE}) {
-    p->bm[c] = (c == QI_CALL_DENOISE && p->kv != QI_KV_BF16) ? QI_ROWS_FP8 : QI_ROWS_BF16;
+    p->bm[c] = QI_ROWS;
     build_tiles(*p, c, tiles[c]);
     std::vector<std::pair<int, int>> items;
     for (int t = 0; t < (int)tiles[c].size(); ++t)
       for (int h = 0; h < p->H; ++h) items.push_back({t, h});
-    // the bf16-source kernel runs one 8-wavefront workgroup per CU; the fp8 one two
-    // 4-wavefront workgroups
-    const bool fp8 = p->bm[c] == QI_ROWS_FP8;
-    build_schedule(*p, tiles[c], items, QI_CUS_PER_XCD * (fp8 ? 2 : 1), !fp8, sched[c]);
+    // the kernel runs one 8-wavefront workgroup per CU
+    build_schedule(*p, tiles[c], items, QI_CUS_PER_XCD, true, sched[c]);
   }
   {
-    p->bm[QI_CALL_FULL] = QI_ROWS_BF16;
+    p->bm[QI_CALL_FULL] = QI_ROWS;
     std::vector<std::pair<int, int>> items;
     std::vector<qi_tile> &ft = tiles[QI_CALL_FULL];
     for (int c : {QI_CALL_PREFIX, QI_CALL_DENOISE}) {

@@ -9,11 +9,10 @@
 
 #include "qi.h"   // include/ of the repository, on the include path
 
-// Attention tiles: rows per workgroup x keys per step.  bf16 key sources run row tiles of
-// up to 256 rows (8 wavefronts x 32 rows; tiles of <= 128 rows split their keys over two
-// wave groups); the fp8-cache kernel runs 128-row tiles (4 wavefronts x 32 rows).
-#define QI_ROWS_BF16 256
-#define QI_ROWS_FP8 128
+// Attention tiles: rows per workgroup x keys per step.  Row tiles of up to 256 rows (8
+// wavefronts x 32 rows; tiles of <= 128 rows split their keys over two wave groups), for
+// every key source and cache type.
+#define QI_ROWS 256
 #define QI_KERNEL_BN 64
 // Number of XCDs of the MI355X and compute units per XCD; workgroups are dealt to the XCDs
 // round-robin in launch order.
