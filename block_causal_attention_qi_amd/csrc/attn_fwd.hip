@@ -174,10 +174,11 @@ __device__ __forceinline__ int tile_kind(int kt, const TileArgs &a) {
 //      is a multiple of 4); ks on l and kib % 4 (D=128) or kib % 2 (D=64).
 // A group of four wavefronts loads either whole tiles (HALF = false) or one half of the
 // rows of each tile (HALF = true, the other group loads the other half); wavefront w of
-// the group issues a run of consecutive K and V instructions.  Instruction indices are wavefront-uniform, so the LDS destination is a
-// scalar; the per-lane part of every global address is a 32-bit offset computed once,
-// added to a scalar base per tile.  Key tiles that straddle the cache/live boundary or
-// kend take a slower per-lane path.
+// the group issues a run of consecutive K and V instructions.  Instruction indices are
+// wavefront-uniform, so the LDS destination is a scalar; the per-lane part of every
+// global address is a 32-bit offset computed once, added to a scalar base per tile.  Key
+// tiles that straddle the cache/live boundary or kend take a slower per-lane path.  Used
+// for bf16 rows only: tiles of an E4M3FN cache tensor go through Coded / sync_tile.
 template <int D, int SRC, bool HALF>
 struct Direct {
   using C = Cfg<D>;
