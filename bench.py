@@ -238,9 +238,8 @@ def main():
         copy_calibration(a.copy_calibration)
         return
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(heads or requests would shard with no exchange; see the design notes)",
-              file=sys.stderr)
+        print("bench.py measures one GPU only: there is no multi-GPU path (heads or "
+              "requests of a wave would shard across GPUs with no exchange)", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
