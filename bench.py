@@ -128,8 +128,60 @@ def capture(fn):
     return g
 
 
+def current_sclk_mhz(text):
+    """The current level of a pp_dpm_sclk listing (the line marked '*', e.g. "1: 2152Mhz *"),
+    in MHz, or None."""
+    for line in text.splitlines():
+        if line.rstrip().endswith("*"):
+            try:
+                return int(line.split(":", 1)[1].strip().split("M")[0])
+            except (ValueError, IndexError):
+                return None
+    return None
+
+
+def sample_clock(fn, seconds=2.0, period=0.02):
+    """The shader clock while fn runs back to back for `seconds`: the current level of the
+    card's pp_dpm_sclk (sysfs; the line marked '*'), read on a host thread every `period`
+    seconds.  None when sysfs does not show exactly one card."""
+    import glob
+    import statistics
+    import threading
+    import torch
+    paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+    if len(paths) != 1:
+        return None
+    vals, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            try:
+                with open(paths[0]) as f:
+                    v = current_sclk_mhz(f.read())
+                if v is not None:
+                    vals.append(v)
+            except OSError:
+                pass
+            stop.wait(period)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        fn()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    if not vals:
+        return None
+    return {"sclk_mhz_median": statistics.median(vals), "sclk_mhz_min": min(vals),
+            "sclk_mhz_max": max(vals), "samples": len(vals), "source": paths[0],
+            "note": "sampled while the timed step ran back to back for %.0f s after the "
+                    "timed region" % seconds}
+
+
 def measure(name, steps, warmup, layers, dev, with_full=False, with_build=True,
-            with_graph=False, kv=None):
+            with_graph=False, kv=None, with_clock=False):
     from block_causal_attention_qi_amd import qi
     L = Layers(name, layers, dev, need_full=with_full, kv=kv)
     flops = qi.useful_flops(L.plan, qi.QI_CALL_DENOISE)
@@ -142,6 +194,8 @@ def measure(name, steps, warmup, layers, dev, with_full=False, with_build=True,
     res.update(ms_per_step=ms / steps, ms_per_layer_step=per_launch,
                tflops=flops / (per_launch * 1e-3) / 1e12)
     res["frac_of_peak"] = res["tflops"] / PEAK_BF16_TFLOPS
+    if with_clock:
+        res["clock"] = sample_clock(L.denoise)
     if with_graph:
         # the whole step (one launch per layer) replayed from a HIP graph: the share of
         # the eager step that is launch overhead
@@ -249,7 +303,7 @@ def main():
     from block_causal_attention_qi_amd import qi  # noqa: F401  (fails loudly if not built)
 
     main_res = measure(a.workload, a.steps, a.warmup, a.layers, dev, with_full=False,
-                       with_graph=True, kv=a.kv)
+                       with_graph=True, kv=a.kv, with_clock=True)
     log("[bench] %s" % json.dumps(main_res))
     extra = {}
     if not a.no_extra:
@@ -308,6 +362,12 @@ def main():
                      "ms_per_launch": round(main_res["ms_per_layer_step"], 5)},
         "extra": extra,
     }
+    clk = main_res.get("clock")
+    if clk:
+        # the published peak scaled to the measured shader clock (it is quoted at 2400 MHz)
+        clk["peak_tflops_at_clock"] = round(PEAK_BF16_TFLOPS * clk["sclk_mhz_median"] / 2400.0, 1)
+        clk["frac_at_clock"] = round(achieved / clk["peak_tflops_at_clock"], 4)
+    out["clock"] = clk
     out["extra"]["graph_replay"] = {
         "workload": a.workload, "ms_per_step": round(main_res["graph_ms_per_step"], 4),
         "tflops": round(main_res["graph_tflops"], 3),

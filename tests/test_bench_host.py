@@ -1,5 +1,6 @@
 """Host-side checks of bench.py that need no GPU: it refuses more than one GPU before it
-touches any device, and it rejects an unknown prefix-cache type."""
+touches any device, it rejects an unknown prefix-cache type, and it reads the shader
+clock from the sysfs level listing."""
 import os
 import subprocess
 import sys
@@ -31,3 +32,12 @@ def test_unknown_cache_type_is_rejected():
     r = _run("--kv", "int4")
     assert r.returncode != 0
     assert "invalid choice" in r.stderr
+
+
+def test_clock_listing_parser():
+    sys.path.insert(0, ROOT)
+    import bench
+    # listings as the sysfs file shows them under load and at idle
+    assert bench.current_sclk_mhz("0: 500Mhz\n1: 2152Mhz *\n2: 2400Mhz\n") == 2152
+    assert bench.current_sclk_mhz("S: 96Mhz *\n0: 500Mhz\n1: 2400Mhz\n") == 96
+    assert bench.current_sclk_mhz("0: 500Mhz\n1: 2400Mhz\n") is None
