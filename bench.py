@@ -95,20 +95,23 @@ class Layers:
                                            t["o_all"])
 
 
-def timed(fn, steps, warmup):
+def timed(fn, steps, warmup, per_step=None):
     """Warm up, then time exactly `steps` calls of fn with HIP events on the current
-    stream (the stream libqi launches on), synchronising on both sides."""
+    stream (the stream libqi launches on), synchronising on both sides.  Returns the total
+    ms; with a list `per_step`, also appends each call's ms (an event after every call)."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record()
-    for _ in range(steps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i in range(steps):
         fn()
-    e.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    return s.elapsed_time(e)   # ms
+    if per_step is not None:
+        per_step.extend(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    return ev[0].elapsed_time(ev[steps])   # ms
 
 
 def capture(fn):
@@ -189,8 +192,12 @@ def measure(name, steps, warmup, layers, dev, with_full=False, with_build=True,
            "head_dim": L.w.head_dim, "kv_cache": L.w.kv_dtype, "layers": layers,
            "denoise_gflop_per_layer": flops / 1e9}
     L.build()   # step 0 of every layer (untimed here: the caches must exist)
-    ms = timed(L.denoise, steps, warmup)
+    each = []
+    ms = timed(L.denoise, steps, warmup, each)
     per_launch = ms / (steps * layers)
+    import statistics
+    res["step_ms"] = {"median": statistics.median(each), "min": min(each), "max": max(each),
+                      "steps": len(each)}
     res.update(ms_per_step=ms / steps, ms_per_layer_step=per_launch,
                tflops=flops / (per_launch * 1e-3) / 1e12)
     res["frac_of_peak"] = res["tflops"] / PEAK_BF16_TFLOPS
@@ -345,6 +352,8 @@ def main():
         "steps": a.steps,
         "warmup": a.warmup,
         "ms_per_step": round(main_res["ms_per_step"], 4),
+        "step_ms": {k: (round(v, 4) if isinstance(v, float) else v)
+                    for k, v in main_res["step_ms"].items()},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
