@@ -98,6 +98,28 @@ def test_ragged_waves(gpu_device, case, kv, d):
     _full_wave_check(x, gpu_device, kv)
 
 
+def _random_wave(i):
+    """Seeded random wave structure: 1..4 requests, 0..4 references each, ragged block
+    lengths (text 1..400, references 1..700, image 1..900 tokens), 1..3 heads."""
+    rng = np.random.default_rng(1000 + i)
+    reqs = []
+    for _ in range(int(rng.integers(1, 5))):
+        n_refs = int(rng.integers(0, 5))
+        reqs.append([int(rng.integers(1, 401))] + [int(v) for v in rng.integers(1, 701, n_refs)]
+                    + [int(rng.integers(1, 901))])
+    return reqs, int(rng.integers(1, 4))
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_waves(gpu_device, i):
+    reqs, h = _random_wave(i)
+    kv = ("bf16", "fp8", "fp8_v")[i % 3]
+    d = (128, 64)[(i // 3) % 2]
+    print("random wave %d: %s heads %d d %d kv %s" % (i, reqs, h, d, kv), flush=True)
+    x = synth.custom(reqs, h, d, kv_dtype=kv, seed=2000 + i)
+    _full_wave_check(x, gpu_device, kv)
+
+
 def _max_wave(seed):
     """QI_MAX_REQUESTS requests with 0..QI_MAX_REFS references each (every count present)
     and short ragged blocks (1..40 tokens)."""
