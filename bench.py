@@ -10,7 +10,12 @@ Prints ONE JSON line.  `value` is useful attention TFLOP/s (4*D*H*allowed pairs;
 pairs are not counted) on the 1024x1024 text-to-image workload (24 heads x 128, text 256
 + image 4096 tokens); the 2048x2048 edit and the others are reported under "extra".
 
-    python bench.py [--steps K] [--warmup W] [--workload t2i1024] [--kv fp8] [--extra] [--no-cpu]
+The default run also times the 2048x2048 edit (the metric's second configuration), the
+four-reference edit cached vs full recompute, and the eight-request fp8 wave (its HBM
+rate over the compulsory bytes); they are summarised under "north_star".
+
+    python bench.py [--steps K] [--warmup W] [--workload t2i1024] [--kv fp8] [--extra]
+                    [--no-extra] [--profile-run] [--no-cpu]
 """
 from __future__ import annotations
 
@@ -28,6 +33,9 @@ METRIC = "block-causal attn TFLOP/s & % MFMA peak per denoise step (1024^2, 2048
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published (no sparsity)
 KERNEL_SRC = os.path.join(ROOT, "block_causal_attention_qi_amd", "csrc", "attn_fwd.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_denoise_t2i1024_traffic.json")
+# (heads, share of the image rows) on which the oracle is timed for the other measured
+# configurations: a few seconds of host work each
+ORACLE_SAMPLES = {"edit2048": (1, 0.25), "edit4": (2, 1.0), "wave8": (1, 0.25)}
 
 
 def log(*a):
@@ -43,7 +51,7 @@ class Layers:
     """Per-layer device buffers of one workload: layer l holds the base inputs rolled by
     97*l tokens (same distribution, different bytes)."""
 
-    def __init__(self, name, layers, dev, need_full=False, kv=None):
+    def __init__(self, name, layers, dev, need_full=False, kv=None, x=None):
         import dataclasses
         import torch
         from block_causal_attention_qi_amd import qi, synth
@@ -51,9 +59,10 @@ class Layers:
         if kv is not None:
             self.w = dataclasses.replace(self.w, kv_dtype=kv)
         w = self.w
-        t0 = time.time()
-        x = synth.generate(w, steps=1)
-        log("[bench] %s: inputs drawn in %.1fs" % (name, time.time() - t0))
+        if x is None:
+            t0 = time.time()
+            x = synth.generate(w, steps=1)
+            log("[bench] %s: inputs drawn in %.1fs" % (name, time.time() - t0))
         b = lambda a: synth.to_bf16(a, dev)
         base = dict(q_pre=b(x.q_pre), k_pre=b(x.k_pre), v_pre=b(x.v_pre), q_img=b(x.q_img[0]),
                     k_img=b(x.k_img[0]), v_img=b(x.v_img[0]))
@@ -183,14 +192,42 @@ def sample_clock(fn, seconds=2.0, period=0.02):
                     "timed region" % seconds}
 
 
-def measure(name, steps, warmup, layers, dev, with_full=False, with_build=True,
-            with_graph=False, kv=None, with_clock=False):
+def kernel_label(head_dim, kv):
+    """Name of the attention kernel instance a denoising call runs."""
+    return "attn_pp_kernel<%d, %s cache>" % (head_dim, kv)
+
+
+def compulsory_bytes(plan, w):
+    """Algorithmic bytes of one denoising launch: image Q, K, V read and O written (bf16),
+    plus the prefix cache read once (bf16: 2 bytes per K and V element; fp8: 1; fp8_v: 2
+    for K, 1 for V) and the fp8 scales."""
     from block_causal_attention_qi_amd import qi
-    L = Layers(name, layers, dev, need_full=with_full, kv=kv)
+    pre, img, _ = qi.qi_plan_tokens(plan)
+    hd = w.n_heads * w.head_dim
+    per_tok = {"bf16": 4, "fp8": 2, "fp8_v": 3}[w.kv_dtype]
+    scales = 0 if w.kv_dtype == "bf16" else 8 * w.n_heads * len(w.requests)
+    return 4 * img * hd * 2 + per_tok * pre * hd + scales
+
+
+def measure(name, steps, warmup, layers, dev, with_full=False, with_build=True,
+            with_graph=False, kv=None, with_clock=False, oracle_sample=None):
+    """Time the denoising step of workload `name` (and optionally its build, graph replay,
+    full recompute and clock).  oracle_sample = (heads, row fraction): also time the fp64
+    oracle on that sample of the same inputs on the host, before the GPU work."""
+    from block_causal_attention_qi_amd import qi, synth
+    t0 = time.time()
+    x = synth.generate(synth.WORKLOADS[name], steps=1)
+    log("[bench] %s: inputs drawn in %.1fs" % (name, time.time() - t0))
+    cpu = oracle_time(name, x, *oracle_sample) if oracle_sample else None
+    L = Layers(name, layers, dev, need_full=with_full, kv=kv, x=x)
+    del x
     flops = qi.useful_flops(L.plan, qi.QI_CALL_DENOISE)
     res = {"workload": name, "requests": L.w.requests, "heads": L.w.n_heads,
            "head_dim": L.w.head_dim, "kv_cache": L.w.kv_dtype, "layers": layers,
+           "kernel": kernel_label(L.w.head_dim, L.w.kv_dtype),
            "denoise_gflop_per_layer": flops / 1e9}
+    if cpu:
+        res["oracle_cpu"] = dict(cpu, tflops=flops / cpu["seconds_per_layer_step"] / 1e12)
     L.build()   # step 0 of every layer (untimed here: the caches must exist)
     each = []
     ms = timed(L.denoise, steps, warmup, each)
@@ -221,49 +258,125 @@ def measure(name, steps, warmup, layers, dev, with_full=False, with_build=True,
         fms = timed(L.full, max(1, steps // 2), 1) / (max(1, steps // 2) * layers)
         res.update(full_ms_per_layer=fms, full_tflops=fflops / (fms * 1e-3) / 1e12,
                    cached_speedup_vs_full=fms / per_launch)
-    if L.w.kv_dtype != "bf16":
-        # compulsory bytes of one denoising launch: image Q/K/V read + O written (bf16)
-        # plus the prefix cache read once (fp8: 1 byte for K and V; fp8_v: 2 for K, 1 for V)
-        pre, img, _ = qi.qi_plan_tokens(L.plan)
-        hd = L.w.n_heads * L.w.head_dim
-        per_tok = 2 if L.w.kv_dtype == "fp8" else 3
-        byts = 4 * img * hd * 2 + per_tok * pre * hd + 8 * L.w.n_heads * len(L.w.requests)
-        res["compulsory_gb_per_s"] = byts / (per_launch * 1e-3) / 1e9
+    byts = compulsory_bytes(L.plan, L.w)
+    res["compulsory_bytes_per_launch"] = byts
+    res["compulsory_gb_per_s"] = byts / (per_launch * 1e-3) / 1e9
     del L
     import torch
     torch.cuda.empty_cache()
     return res
 
 
-def cpu_baseline(name):
-    """The fp64 oracle (oracle/attention.py, untuned) on one layer-step of the cached
-    denoising call, all heads and rows, on the host cores."""
+def host_info():
+    """The host the oracle runs on: logical CPUs, the BLAS library NumPy calls and its
+    thread count, and the thread variables of the environment."""
+    info = {"os_cpu_count": os.cpu_count(),
+            "env": {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS",
+                                                   "MKL_NUM_THREADS")}}
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if blas:
+            info["blas"] = {"library": blas[0].get("internal_api"),
+                            "version": blas[0].get("version"),
+                            "threads": blas[0].get("num_threads"),
+                            "file": os.path.basename(blas[0].get("filepath") or "")}
+    except Exception:   # threadpoolctl missing: the BLAS stays unnamed
+        pass
+    return info
+
+
+def oracle_time(name, x, heads=None, row_frac=1.0, min_seconds=0.0, max_reps=1):
     import numpy as np
+    """Seconds of the fp64 oracle (oracle/attention.py, untuned) for one layer-step of the
+    cached denoising call of workload `name` with inputs x: every request, on the first
+    `heads` heads (all by default) and the first row_frac of each request's image rows,
+    scaled by H / heads / row_frac (the oracle computes every row and head on its own, so
+    its time is linear in both).  Repeated until min_seconds have passed or max_reps runs
+    were made."""
     from block_causal_attention_qi_amd import synth
     from oracle import attention as A
+    w = synth.WORKLOADS[name]
+    nh = w.n_heads if heads is None else min(heads, w.n_heads)
+    e = lambda a: synth.bf16_exact(a[:, :nh])
+    args, rows = [], 0
+    po = io = 0
+    for bl in w.requests:
+        lp, ni = sum(bl[:-1]), bl[-1]
+        nr = max(1, int(round(ni * row_frac)))
+        rows += nr
+        args.append((bl, e(x.q_img[0][io:io + nr]), e(x.k_pre[po:po + lp]),
+                     e(x.v_pre[po:po + lp]), e(x.k_img[0][io:io + ni]),
+                     e(x.v_img[0][io:io + ni])))
+        po += lp
+        io += ni
+    reps, t0 = 0, time.perf_counter()
+    while reps < 1 or (time.perf_counter() - t0 < min_seconds and reps < max_reps):
+        for bl, q, kp, vp, ki, vi in args:
+            lp = sum(bl[:-1])
+            # the image rows kept: the first q.shape[0] of the block, over every key
+            mask = A.allowed_mask(bl, rows=range(lp, lp + q.shape[0]))
+            A.masked_attention(q, np.concatenate([kp, ki]), np.concatenate([vp, vi]), mask)
+        reps += 1
+    elapsed = (time.perf_counter() - t0) / reps
+    scale = (w.n_heads / nh) * (sum(w.image_lens) / rows)
+    return {"seconds_per_layer_step": elapsed * scale, "measured_seconds": elapsed,
+            "repetitions": reps,
+            "sample": "heads 0..%d of %d and %d of %d image rows (the first of each request), "
+                      "every key, float64 NumPy oracle; time scaled by %.3g to the whole "
+                      "layer-step" % (nh - 1, w.n_heads, rows, sum(w.image_lens), scale)}
+
+
+def cpu_baseline(name, others):
+    """The oracle on the host cores: one whole layer-step of the main workload's denoising
+    call (all heads, all image rows, repeated for about 10 s), plus the samples timed for
+    the other configurations (others: workload -> the oracle_cpu record of its measure)."""
+    from block_causal_attention_qi_amd import synth
     from oracle import layout as OL
     w = synth.WORKLOADS[name]
     x = synth.generate(w, steps=1)
-    e = lambda a: synth.bf16_exact(a)
-    bl = w.requests[0]
-    args = (e(x.q_img[0]), e(x.k_pre), e(x.v_pre), e(x.k_img[0]), e(x.v_img[0]))
-    reps, t0 = 0, time.perf_counter()
-    while reps < 1 or (time.perf_counter() - t0 < 10.0 and reps < 8):
-        A.denoise_step(bl, *args)    # repeated until about 10 s of CPU work
-        reps += 1
-    dt = (time.perf_counter() - t0) / reps
+    rec = oracle_time(name, x, min_seconds=10.0, max_reps=8)
+    del x
+    dt = rec["seconds_per_layer_step"]
     flops = OL.useful_flops(w.requests, OL.CALL_DENOISE, w.n_heads, w.head_dim)
-    threads = None
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads") or 0) for i in threadpool_info()) or None
-    except Exception:
-        pass
+    host = host_info()
+    threads = (host.get("blas") or {}).get("threads")
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads or os.cpu_count(),
-            "kind": "oracle", "seconds_per_layer_step": dt, "repetitions": reps,
+            "kind": "oracle", "seconds_per_layer_step": dt, "repetitions": rec["repetitions"],
             "sample": "one layer-step of the denoising call of %s (all %d heads, all %d image "
-                      "rows), float64 NumPy oracle, repeated %d times" % (
-                          name, w.n_heads, w.image_lens[0], reps)}
+                      "rows), float64 NumPy oracle, repeated %d times; cores = threads of the "
+                      "BLAS the oracle calls" % (name, w.n_heads, sum(w.image_lens),
+                                                 rec["repetitions"]),
+            "host": host, "other_configs": others}
+
+
+def provenance():
+    """Device, runtime and source identity of the run."""
+    import glob
+    import subprocess
+    import torch
+    rocm = None
+    for f in ("/opt/rocm/.info/version",):
+        try:
+            with open(f) as fh:
+                rocm = fh.read().strip()
+        except OSError:
+            pass
+    try:
+        git = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True,
+                             text=True, timeout=10).stdout.strip() or None
+    except (OSError, subprocess.SubprocessError):
+        git = None
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "block_causal_attention_qi_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode() + b"\0" + fh.read())
+    props = torch.cuda.get_device_properties(0)
+    return {"device": torch.cuda.get_device_name(0),
+            "gcn_arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count,
+            "rocm": rocm, "torch_hip": torch.version.hip, "torch": torch.__version__,
+            "git_commit": git, "csrc_sha256": h.hexdigest()[:16]}
 
 
 def copy_calibration(nbytes):
@@ -288,9 +401,13 @@ def main():
     ap.add_argument("--kv", choices=["bf16", "fp8", "fp8_v"], default=None,
                     help="prefix cache type of the main workload (default: the workload's own)")
     ap.add_argument("--extra", action="store_true",
-                    help="also time edit4 (cached vs full), wave8 (fp8) and edit10 (ten "
-                         "references: cached vs full, and the fp8 / fp8_v caches)")
+                    help="also time true CFG (edit1 vs cfg_edit1) and edit10 (ten references: "
+                         "cached vs full, and the fp8 / fp8_v caches)")
     ap.add_argument("--no-extra", action="store_true", help="time only the main workload")
+    ap.add_argument("--profile-run", action="store_true",
+                    help="only the main workload's timed denoising steps (no build timing, "
+                         "graph replay or clock sampling), so that a profiler's average for "
+                         "the denoising kernel covers exactly the launches the line reports")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (profiler byte-counter scale)")
@@ -309,16 +426,20 @@ def main():
     dev = torch.device("cuda:0")
     from block_causal_attention_qi_amd import qi  # noqa: F401  (fails loudly if not built)
 
+    lean = a.profile_run
     main_res = measure(a.workload, a.steps, a.warmup, a.layers, dev, with_full=False,
-                       with_graph=True, kv=a.kv, with_clock=True)
+                       with_build=not lean, with_graph=not lean, kv=a.kv, with_clock=not lean)
     log("[bench] %s" % json.dumps(main_res))
     extra = {}
-    if not a.no_extra:
-        names = ["edit2048"] + (["edit4", "wave8"] if a.extra else [])
-        for n in names:
+    if not (a.no_extra or lean):
+        # the second metric configuration, the cached-vs-full ratio on the four-reference
+        # edit and the fp8 wave's HBM rate
+        for n in ("edit2048", "edit4", "wave8"):
             if n == a.workload:
                 continue
-            extra[n] = measure(n, max(2, a.steps // 2), 1, a.layers, dev, with_full=(n == "edit4"))
+            sample = None if a.no_cpu else ORACLE_SAMPLES[n]
+            extra[n] = measure(n, max(2, a.steps // 2), 1, a.layers, dev, with_full=(n == "edit4"),
+                               oracle_sample=sample)
             log("[bench] %s" % json.dumps(extra[n]))
         if a.extra:
             # true CFG: both branches in one wave against the positive branch alone
@@ -338,7 +459,9 @@ def main():
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
-        if rec.get("kernel_source_sha256") == kernel_sha() and rec.get("workload") == a.workload:
+        if (rec.get("kernel_source_sha256") == kernel_sha() and rec.get("workload") == a.workload
+                and rec.get("kv_cache") == main_res["kv_cache"]
+                and rec.get("head_dim") == main_res["head_dim"]):
             traffic = rec["hbm_bytes_per_launch"]
     except (OSError, ValueError, KeyError):
         pass
@@ -366,24 +489,39 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "kernel": "attn_pp_kernel<128, bf16 cache>",
+                     "kernel": main_res["kernel"],
                      "flop_per_launch": flops_launch,
-                     "ms_per_launch": round(main_res["ms_per_layer_step"], 5)},
+                     "ms_per_launch": round(main_res["ms_per_layer_step"], 5),
+                     "algorithmic_bytes_per_launch": main_res["compulsory_bytes_per_launch"]},
         "extra": extra,
+        "provenance": provenance(),
     }
+    summary = {}
+    if "edit2048" in extra:
+        summary["edit2048_tflops"] = round(extra["edit2048"]["tflops"], 1)
+        summary["edit2048_frac_of_peak"] = round(extra["edit2048"]["frac_of_peak"], 4)
+    if "edit4" in extra:
+        summary["edit4_cached_speedup_vs_full"] = round(extra["edit4"]["cached_speedup_vs_full"], 3)
+    if "wave8" in extra:
+        summary["wave8_fp8_compulsory_gb_per_s"] = round(extra["wave8"]["compulsory_gb_per_s"], 1)
+        summary["wave8_fp8_tflops"] = round(extra["wave8"]["tflops"], 1)
+    if summary:
+        out["north_star"] = summary
     clk = main_res.get("clock")
     if clk:
         # the published peak scaled to the measured shader clock (it is quoted at 2400 MHz)
         clk["peak_tflops_at_clock"] = round(PEAK_BF16_TFLOPS * clk["sclk_mhz_median"] / 2400.0, 1)
         clk["frac_at_clock"] = round(achieved / clk["peak_tflops_at_clock"], 4)
     out["clock"] = clk
-    out["extra"]["graph_replay"] = {
-        "workload": a.workload, "ms_per_step": round(main_res["graph_ms_per_step"], 4),
-        "tflops": round(main_res["graph_tflops"], 3),
-        "launch_overhead_share": round(main_res["launch_overhead_share"], 4),
-        "note": "the same %d-layer step captured once in a HIP graph and replayed" % a.layers}
+    if "graph_ms_per_step" in main_res:
+        out["extra"]["graph_replay"] = {
+            "workload": a.workload, "ms_per_step": round(main_res["graph_ms_per_step"], 4),
+            "tflops": round(main_res["graph_tflops"], 3),
+            "launch_overhead_share": round(main_res["launch_overhead_share"], 4),
+            "note": "the same %d-layer step captured once in a HIP graph and replayed" % a.layers}
     if not a.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(a.workload)
+        others = {n: r["oracle_cpu"] for n, r in extra.items() if "oracle_cpu" in r}
+        out["cpu_baseline"] = cpu_baseline(a.workload, others)
         if main_res["kv_cache"] != "bf16":
             out["cpu_baseline"]["sample"] += " (bf16 prefix values, not the %s cache)" % main_res["kv_cache"]
         log("[bench] cpu baseline %s" % json.dumps(out["cpu_baseline"]))

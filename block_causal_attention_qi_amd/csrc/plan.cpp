@@ -408,6 +408,33 @@ qi_status qi_plan_tile_map(const qi_plan *p, int32_t call, int32_t bm, int32_t b
   return QI_OK;
 }
 
+qi_status qi_plan_launch_items(const qi_plan *p, int32_t call, int32_t *host_out, size_t n,
+                               size_t *n_needed) {
+  if (!p || call < 0 || call > 2) return QI_ERR_INVALID_ARG;
+  const size_t len = (size_t)p->sched_len[call];
+  if (n_needed) *n_needed = 4 * len;
+  if (!host_out || n < 4 * len) return QI_ERR_BUFFER_TOO_SMALL;
+  const int32_t *sched = reinterpret_cast<const int32_t *>(p->ws_image.data() + p->sched_off[call]);
+  const qi_tile *tiles = reinterpret_cast<const qi_tile *>(p->ws_image.data() + p->tiles_off[call]);
+  for (size_t i = 0; i < len; ++i) {
+    int32_t *e = host_out + 4 * i;
+    const int32_t code = sched[i];
+    if (code < 0) {
+      e[0] = e[1] = e[2] = e[3] = -1;
+      continue;
+    }
+    const qi_tile &t = tiles[code / p->H];
+    const qi_req_host &rq = p->req[t.req];
+    const int32_t base = call == QI_CALL_PREFIX ? rq.pre_tok
+                         : call == QI_CALL_DENOISE ? rq.img_tok - rq.lp : rq.all_tok;
+    e[0] = t.req;
+    e[1] = code % p->H;
+    e[2] = t.q_tok - base;
+    e[3] = t.nrows;
+  }
+  return QI_OK;
+}
+
 qi_status qi_plan_cache_offset(const qi_plan *p, int32_t req, int32_t kv, int32_t head,
                                int32_t tok, size_t *byte_off) {
   if (!p || !byte_off || req < 0 || req >= p->n_req || kv < 0 || kv > 2) return QI_ERR_INVALID_ARG;

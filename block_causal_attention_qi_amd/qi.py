@@ -23,7 +23,7 @@ QI_MAX_REQUESTS, QI_MAX_REFS, QI_MAX_HEADS = 64, 10, 128
 
 EXPORTS = ("qi_plan_create", "qi_plan_destroy", "qi_plan_sizes", "qi_plan_upload",
            "qi_prefix_kv_build", "qi_denoise_attn_step", "qi_attn_full_reference_step",
-           "qi_plan_tile_map", "qi_plan_kernel_tile", "qi_plan_cache_offset",
+           "qi_plan_tile_map", "qi_plan_kernel_tile", "qi_plan_launch_items", "qi_plan_cache_offset",
            "qi_plan_pairs", "qi_plan_tokens", "qi_status_string")
 
 
@@ -60,6 +60,7 @@ def _load():
         "qi_attn_full_reference_step": ([P, VP, VP, VP, VP, VP], I32),
         "qi_plan_tile_map": ([P, I32, I32, I32, VP, SZ, ctypes.POINTER(SZ)], I32),
         "qi_plan_kernel_tile": ([P, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)], I32),
+        "qi_plan_launch_items": ([P, I32, VP, SZ, ctypes.POINTER(SZ)], I32),
         "qi_plan_cache_offset": ([P, I32, I32, I32, I32, ctypes.POINTER(SZ)], I32),
         "qi_plan_pairs": ([P, I32, ctypes.POINTER(I64)], I32),
         "qi_plan_tokens": ([P, ctypes.POINTER(I64), ctypes.POINTER(I64), ctypes.POINTER(I64)], I32),
@@ -235,6 +236,19 @@ def qi_plan_kernel_tile(plan, call):
     _check(lib.qi_plan_kernel_tile(plan.handle, call, ctypes.byref(bm), ctypes.byref(bn)),
            "qi_plan_kernel_tile")
     return bm.value, bn.value
+
+
+def qi_plan_launch_items(plan, call):
+    """Launch schedule of a call: int32 array [workgroups, 4] of (request, head, first
+    row as a position in the request's sequence, row count); padding rows are -1."""
+    need = ctypes.c_size_t()
+    st = lib.qi_plan_launch_items(plan.handle, call, None, 0, ctypes.byref(need))
+    if st not in (QI_OK, QI_ERR_BUFFER_TOO_SMALL):
+        _check(st, "qi_plan_launch_items")
+    out = np.zeros(max(4, need.value), dtype=np.int32)
+    _check(lib.qi_plan_launch_items(plan.handle, call, out.ctypes.data_as(ctypes.c_void_p),
+                                    out.size, ctypes.byref(need)), "qi_plan_launch_items")
+    return out[:need.value].reshape(-1, 4)
 
 
 def qi_plan_cache_offset(plan, req, kv, head, tok):

@@ -121,7 +121,11 @@ qi_status qi_plan_upload(qi_plan *plan, void *d_workspace, size_t workspace_byte
 
 /* Step 0, prefix side: write the prefix cache from k_pre/v_pre (bf16 copy, or fp8
  * quantisation as described above) and compute block-causal attention of the prefix rows
- * over the prefix keys into o_pre.  q/k/v/o_pre: [sum L_p][H][D] bf16.  Fully overwrites
+ * over the prefix keys into o_pre.  The prompt and reference K/V computed at the first
+ * step is what every later step reuses (ThakiCloud blog "Qwen-Image-2.1 vLLM-Omni day 0",
+ * section "Serving architecture: the cross-step prefix KV cache"); the prefill runs once,
+ * eagerly (vLLM recipe "Qwen/Qwen-Image-2.1", section "CUDA graphs"); FP8 storage is the
+ * recipe's "fp8" / "fp8_v" option (section "Prefix KV cache").  q/k/v/o_pre: [sum L_p][H][D] bf16.  Fully overwrites
  * every request's region of d_cache (the cache is rebuilt per generation).  Requests
  * without a prefix cannot occur (the text block is never empty). */
 qi_status qi_prefix_kv_build(qi_plan *plan, const void *q_pre, const void *k_pre,
@@ -129,7 +133,10 @@ qi_status qi_prefix_kv_build(qi_plan *plan, const void *q_pre, const void *k_pre
                              size_t cache_bytes, void *stream);
 
 /* Denoising step: attention of the image rows over the cached prefix keys followed by the
- * live image keys of the same request.  q/k/v/o_img: [sum N_img][H][D] bf16.  Reads the
+ * live image keys of the same request -- the remaining steps reuse the cached prefix K/V
+ * exactly and recompute only the image rows (vLLM recipe "Qwen/Qwen-Image-2.1", section
+ * "Prefix KV cache"; ThakiCloud blog, section "Serving architecture: the cross-step prefix
+ * KV cache"); requests at the same phase share one launch (recipe, "Online serving").  q/k/v/o_img: [sum N_img][H][D] bf16.  Reads the
  * cache only.  QI_ERR_STATE if no qi_prefix_kv_build has been enqueued on this plan.  On
  * a bf16 cache the result is bit-identical to the image rows of
  * qi_attn_full_reference_step on the same values (same tiles, same arithmetic). */
@@ -138,7 +145,11 @@ qi_status qi_denoise_attn_step(const qi_plan *plan, const void *d_cache, size_t 
                                void *o_img, void *stream);
 
 /* Full recompute without the cache: every row of every request over that request's keys,
- * block-causal, fully masked key tiles skipped.  q/k/v/o_all: [sum N][H][D] bf16.  Used
+ * block-causal, fully masked key tiles skipped -- the no-cache baseline whose work the
+ * prefix cache cuts (about a fifth of the sequence is recomputed with four references:
+ * vLLM recipe "Qwen/Qwen-Image-2.1", section "Prefix KV cache"), and the check that the
+ * cached step is exact (ThakiCloud blog, section "Serving architecture: the cross-step
+ * prefix KV cache": block-causal attention is what makes the reuse exact).  q/k/v/o_all: [sum N][H][D] bf16.  Used
  * to show that reuse is exact. */
 qi_status qi_attn_full_reference_step(const qi_plan *plan, const void *q_all,
                                       const void *k_all, const void *v_all, void *o_all,
@@ -159,6 +170,18 @@ qi_status qi_plan_tile_map(const qi_plan *plan, int32_t call, int32_t bm, int32_
  * halves see the same key tiles, so the map is unchanged); the full call runs each row
  * exactly as the prefix or denoising call runs it. */
 qi_status qi_plan_kernel_tile(const qi_plan *plan, int32_t call, int32_t *bm, int32_t *bn);
+
+/* The launch schedule of a call: one record of four int32 per workgroup, in launch order
+ * (workgroup i runs on XCD i % 8): request, head, first row, row count.  The first row
+ * is a position in the request's sequence (text, references, image; 0-based), so a
+ * denoising item starts at L_p or later.  Padding workgroups, which do no work, read
+ * -1 -1 -1 -1.  Row counts above half the kernel's row tile run on the kernel's
+ * whole-tile path; the others (half tiles the schedule split off, short block tails) run
+ * with the key tiles split over two wavefront groups.  Writes into host_out (host
+ * memory) when n >= 4 * workgroups; *n_needed (may be NULL) receives that count.
+ * QI_ERR_BUFFER_TOO_SMALL if host_out is NULL or n is too small. */
+qi_status qi_plan_launch_items(const qi_plan *plan, int32_t call, int32_t *host_out, size_t n,
+                               size_t *n_needed);
 
 /* Byte offset in the cache arena of element (request, kv = 0 K | 1 V, head, token,
  * channel 0); for kv = 2 the offset of the request's float32 scales [2][H] (fp8 only). */

@@ -13,7 +13,13 @@ from oracle import fp8 as F
 from oracle import layout as L
 
 BF16_MAXABS, BF16_RELRMS = 2e-2, 5e-3     # bf16 path bar
-FP8_MAXABS, FP8_RELRMS = 8e-2, 2e-2       # fp8 prefix-cache path bar
+# fp8 prefix caches: the stated fp8-path bar, and the bar the kernel meets against the
+# oracle run on the dequantised cache (code x scale), whose only extra error is bf16
+# rounding, the same as the bf16 path's.  E4M3 quantisation alone moves the output by
+# 2-4e-2 rel-RMS from the unquantised prefix (oracle against oracle), so that distance
+# is reported and bounded by the quantisation's own distance plus the bf16 bar.
+FP8_MAXABS, FP8_RELRMS = 8e-2, 2e-2
+FP8_DEQ_MAXABS, FP8_DEQ_RELRMS = BF16_MAXABS, BF16_RELRMS
 
 
 def say(*a):
@@ -141,14 +147,23 @@ def oracle_rows(w, call, e, rows_per_req, kv="bf16", heads=None):
     return res
 
 
-def sample_rows(bl, call, bm, rng, n_random):
-    """Call-relative rows: first/last rows of every block and row tile, plus random rows."""
+def sample_rows(bl, call, bm, rng, n_random, items=None, req=0):
+    """Call-relative rows: first/last rows of every block and row tile, the rows where a
+    wavefront's 32 or 64 rows start inside every launched item (items: the call's
+    launch schedule from qi_plan_launch_items, whose split halves start at row 128 of a
+    tile), plus random rows."""
     lp = sum(bl[:-1])
     tiles = L.row_tiles(bl, call, bm)
     base = lp if call == L.CALL_DENOISE else 0
     rows = set()
     for r0, nr in tiles:
         rows.update({r0 - base, r0 + nr - 1 - base, r0 + min(nr - 1, 31) - base})
+    if items is not None:
+        for r, _, r0, nr in items:
+            if r != req:
+                continue
+            for off in (0, 31, 32, 63, 64, nr - 1):
+                rows.add(int(r0 + min(off, nr - 1) - base))
     total = sum(nr for _, nr in tiles)
     rows.update(int(x) for x in rng.integers(0, total, n_random))
     return sorted(rows)

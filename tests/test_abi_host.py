@@ -157,3 +157,53 @@ def test_calls_rejected_before_any_launch():
     with pytest.raises(qi.QiError):
         _ = p.handle
 
+
+
+@pytest.mark.parametrize("reqs,h,d", WAVES)
+def test_launch_schedule_covers_every_row_once(reqs, h, d):
+    """Every (request, head, row) of a call is computed by exactly one workgroup; items
+    never cross a block and hold at most the kernel's row tile; the full call runs each
+    row in the same item shape as the prefix or denoising call (the reason reuse is
+    bit-exact); workgroup i runs on XCD i % 8, and items of one (request, head) stay on
+    one XCD."""
+    p = qi.Plan(reqs, h, d)
+    shapes = {}
+    for call in (qi.QI_CALL_PREFIX, qi.QI_CALL_DENOISE, qi.QI_CALL_FULL):
+        items = qi.qi_plan_launch_items(p, call)
+        bm, _ = qi.qi_plan_kernel_tile(p, call)
+        assert len(items) % 8 == 0
+        pad = items[:, 0] < 0
+        assert np.all(items[pad] == -1)
+        seen = [np.zeros((sum(bl), h), np.int32) for bl in reqs]
+        xcd = {}
+        for i, e in enumerate(items):
+            r, hh, r0, nr = (int(v) for v in e)
+            if r < 0:
+                continue
+            bl = reqs[r]
+            ends = np.cumsum(bl)
+            b = int(np.searchsorted(ends, r0, side="right"))
+            assert 1 <= nr <= bm and r0 + nr <= ends[b], "item crosses a block"
+            if call == qi.QI_CALL_PREFIX:
+                assert b < len(bl) - 1
+            elif call == qi.QI_CALL_DENOISE:
+                assert b == len(bl) - 1
+            seen[r][r0:r0 + nr, hh] += 1
+            assert xcd.setdefault((r, hh), i % 8) == i % 8
+            key = (r, hh, r0)
+            if call == qi.QI_CALL_FULL:
+                assert shapes[key] == nr
+            else:
+                shapes[key] = nr
+        for r, bl in enumerate(reqs):
+            lp = sum(bl[:-1])
+            rows = {qi.QI_CALL_PREFIX: slice(0, lp), qi.QI_CALL_DENOISE: slice(lp, sum(bl)),
+                    qi.QI_CALL_FULL: slice(0, sum(bl))}[call]
+            assert np.all(seen[r][rows] == 1)
+            assert np.all(np.delete(seen[r], np.arange(sum(bl))[rows], axis=0) == 0)
+    n = ctypes.c_size_t()
+    assert qi.lib.qi_plan_launch_items(p.handle, 3, None, 0, ctypes.byref(n)) == \
+        qi.QI_ERR_INVALID_ARG
+    assert qi.lib.qi_plan_launch_items(p.handle, 1, None, 0, ctypes.byref(n)) == \
+        qi.QI_ERR_BUFFER_TOO_SMALL
+    assert n.value == 4 * len(qi.qi_plan_launch_items(p, 1))

@@ -10,11 +10,13 @@ replay must read the inputs' current contents.
 """
 from __future__ import annotations
 
+import numpy as np
 import pytest
 import torch
 
 from block_causal_attention_qi_amd import qi, synth
-from qi_gpu import GpuWave, say
+from oracle import layout as L
+from qi_gpu import BF16_MAXABS, BF16_RELRMS, GpuWave, check, exact_inputs, f64, oracle_rows, say
 
 pytestmark = pytest.mark.gpu
 
@@ -61,6 +63,14 @@ def test_graph_replay_matches_eager(gpu_device, kv):
         for l, (o, r) in enumerate(zip(outs, ref)):
             assert torch.equal(bits(o), bits(r)), ("replay", rep, "layer", l)
         say("  replay %d matches eager (%s cache)" % (rep, kv))
+        if rep == 0:
+            # the replayed step against the fp64 oracle, every element of every layer (an
+            # fp8 cache against the oracle run on the dequantised cache, at the bf16 bar)
+            for l, (gw, o) in enumerate(zip(layers, outs)):
+                w = gw.w
+                rows = [list(range(n)) for n in w.image_lens]
+                want = np.concatenate(oracle_rows(w, L.CALL_DENOISE, exact_inputs(gw.x), rows, kv))
+                check(f64(o), want, BF16_MAXABS, BF16_RELRMS, "graph replay layer %d vs oracle" % l)
 
     # new image inputs in the captured buffers: the replay reads them
     q0, k0, v0 = layers[0].img[0]
