@@ -40,7 +40,34 @@ qi_status qi_prefix_kv_build(qi_plan *p, const void *q_pre, const void *k_pre,
     return QI_ERR_INVALID_ARG;
   if (!p->d_ws) return QI_ERR_STATE;
   if (cache_bytes < p->cache_bytes) return QI_ERR_BUFFER_TOO_SMALL;
-  qi_status st = qi_launch_cache_write(p, k_pre, v_pre, d_cache, stream);
+  qi_status st = qi_launch_cache_write(p, k_pre, v_pre, d_cache, nullptr, stream);
+  if (st != QI_OK) return st;
+  st = qi_launch_attention(p, QI_CALL_PREFIX, q_pre, k_pre, v_pre, o_pre, nullptr, stream);
+  if (st != QI_OK) return st;
+  p->built = true;
+  return QI_OK;
+}
+
+// The same step-0 build for callers that cannot allocate device memory: the fp8 absmax
+// partials go to the library's static scratch array of this device instead of the
+// workspace (the workspace still holds the plan's tables, uploaded beforehand).  Nothing
+// in the scratch has to start at zero: the first fp8 pass writes every partial that the
+// later passes read.  Calls that overlap in time on one device share the array and race.
+qi_status qi_prefix_kv_build_noalloc(qi_plan *p, const void *q_pre, const void *k_pre,
+                                     const void *v_pre, void *o_pre, void *d_cache,
+                                     size_t cache_bytes, void *stream) {
+  if (!p || !ok_ptr(q_pre) || !ok_ptr(k_pre) || !ok_ptr(v_pre) || !ok_ptr(o_pre) ||
+      !ok_ptr(d_cache))
+    return QI_ERR_INVALID_ARG;
+  if (p->part_floats > QI_NOALLOC_MAX_PARTIALS) return QI_ERR_BUFFER_TOO_SMALL;
+  if (!p->d_ws) return QI_ERR_STATE;
+  if (cache_bytes < p->cache_bytes) return QI_ERR_BUFFER_TOO_SMALL;
+  float *part = nullptr;
+  if (p->part_floats > 0) {
+    const qi_status st = qi_scratch_partials(&part);
+    if (st != QI_OK) return st;
+  }
+  qi_status st = qi_launch_cache_write(p, k_pre, v_pre, d_cache, part, stream);
   if (st != QI_OK) return st;
   st = qi_launch_attention(p, QI_CALL_PREFIX, q_pre, k_pre, v_pre, o_pre, nullptr, stream);
   if (st != QI_OK) return st;

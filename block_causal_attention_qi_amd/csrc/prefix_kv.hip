@@ -24,9 +24,22 @@
 // The copy and passes 1 and 3 run one workgroup per (64-token chunk, request, head).
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "qi_internal.h"
 
+// Scratch of the allocation-free build (qi_prefix_kv_build_noalloc): the absmax partials
+// of the fp8 passes live here instead of in the caller's workspace.  Each GPU the library
+// runs on holds its own copy until the process ends.  Host code must never pass the name
+// `scratch` to a kernel or a copy (on the host it is only a stand-in symbol): it uses the
+// device address qi_scratch_partials() obtained with hipGetSymbolAddress on that device.
+static __device__ __align__(256) float scratch[QI_NOALLOC_MAX_PARTIALS];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float *g_scratch_ptr[kMaxDevices] = {};
 
 constexpr int NT = 256;
 constexpr int CHUNK = QI_CACHE_CHUNK;
@@ -189,8 +202,21 @@ __global__ __launch_bounds__(NT) void cache_quant_fp8(const qi_req_dev *__restri
 
 }  // namespace
 
+qi_status qi_scratch_partials(float **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QI_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return QI_ERR_HIP;
+    g_scratch_ptr[dev] = static_cast<float *>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return QI_OK;
+}
+
 qi_status qi_launch_cache_write(const qi_plan *p, const void *k_pre, const void *v_pre,
-                                void *cache, void *stream) {
+                                void *cache, float *partials, void *stream) {
   if (p->max_chunks == 0) return QI_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t *ws = static_cast<uint8_t *>(p->d_ws);
@@ -202,7 +228,7 @@ qi_status qi_launch_cache_write(const qi_plan *p, const void *k_pre, const void 
   if (p->kv == QI_KV_BF16) {
     hipLaunchKernelGGL(cache_copy_bf16, grid, dim3(NT), 0, s, reqs, p->H, p->D, k, v, c);
   } else {
-    float *part = reinterpret_cast<float *>(ws + p->part_off);
+    float *part = partials ? partials : reinterpret_cast<float *>(ws + p->part_off);
     hipLaunchKernelGGL(cache_absmax_fp8, grid, dim3(NT), 0, s, reqs, p->H, p->D, k, v, part);
     if (hipGetLastError() != hipSuccess) return QI_ERR_HIP;
     hipLaunchKernelGGL(cache_absmax_reduce, dim3(p->n_req, p->H), dim3(NT), 0, s, reqs, p->H, part);

@@ -82,5 +82,10 @@ inline int qi_cache_elem_bytes(int kv, int which) {
 // Kernel launchers (defined in the .hip files).  Return QI_OK or QI_ERR_HIP.
 qi_status qi_launch_attention(const qi_plan *p, int call, const void *q, const void *k,
                               const void *v, void *o, const void *cache, void *stream);
+// partials: device buffer of the fp8 absmax partials (p->part_floats floats), or null for
+// the workspace's own region.
 qi_status qi_launch_cache_write(const qi_plan *p, const void *k_pre, const void *v_pre,
-                                void *cache, void *stream);
+                                void *cache, float *partials, void *stream);
+// Device address of this device's static scratch (QI_NOALLOC_MAX_PARTIALS floats), looked
+// up once per device with that device current.  QI_ERR_HIP if the lookup fails.
+qi_status qi_scratch_partials(float **out);

@@ -20,9 +20,10 @@ QI_OK, QI_ERR_INVALID_ARG, QI_ERR_UNSUPPORTED, QI_ERR_STATE, QI_ERR_BUFFER_TOO_S
 QI_KV_BF16, QI_KV_FP8_E4M3, QI_KV_FP8_V = 0, 1, 2
 QI_CALL_PREFIX, QI_CALL_DENOISE, QI_CALL_FULL = 0, 1, 2
 QI_MAX_REQUESTS, QI_MAX_REFS, QI_MAX_HEADS = 64, 10, 128
+QI_NOALLOC_MAX_PARTIALS = 262144
 
 EXPORTS = ("qi_plan_create", "qi_plan_destroy", "qi_plan_sizes", "qi_plan_upload",
-           "qi_prefix_kv_build", "qi_denoise_attn_step", "qi_attn_full_reference_step",
+           "qi_prefix_kv_build", "qi_prefix_kv_build_noalloc", "qi_denoise_attn_step", "qi_attn_full_reference_step",
            "qi_plan_tile_map", "qi_plan_kernel_tile", "qi_plan_launch_items", "qi_plan_cache_offset",
            "qi_plan_pairs", "qi_plan_tokens", "qi_status_string")
 
@@ -56,6 +57,7 @@ def _load():
         "qi_plan_sizes": ([P, ctypes.POINTER(SZ), ctypes.POINTER(SZ)], I32),
         "qi_plan_upload": ([P, VP, SZ, VP], I32),
         "qi_prefix_kv_build": ([P, VP, VP, VP, VP, VP, SZ, VP], I32),
+        "qi_prefix_kv_build_noalloc": ([P, VP, VP, VP, VP, VP, SZ, VP], I32),
         "qi_denoise_attn_step": ([P, VP, SZ, VP, VP, VP, VP, VP], I32),
         "qi_attn_full_reference_step": ([P, VP, VP, VP, VP, VP], I32),
         "qi_plan_tile_map": ([P, I32, I32, I32, VP, SZ, ctypes.POINTER(SZ)], I32),
@@ -197,6 +199,18 @@ def qi_prefix_kv_build(plan, q_pre, k_pre, v_pre, o_pre, cache, stream=None):
                                   _ptr(k_pre, "k_pre", bf, n), _ptr(v_pre, "v_pre", bf, n),
                                   _ptr(o_pre, "o_pre", bf, n), _ptr(cache, "cache", torch.uint8),
                                   cache.numel(), _stream(stream)), "qi_prefix_kv_build")
+
+
+def qi_prefix_kv_build_noalloc(plan, q_pre, k_pre, v_pre, o_pre, cache, stream=None):
+    """qi_prefix_kv_build whose fp8 absmax partials use the library's static scratch."""
+    import torch
+    n = _live_numel(plan, QI_CALL_PREFIX)
+    bf = torch.bfloat16
+    _check(lib.qi_prefix_kv_build_noalloc(plan.handle, _ptr(q_pre, "q_pre", bf, n),
+                                          _ptr(k_pre, "k_pre", bf, n), _ptr(v_pre, "v_pre", bf, n),
+                                          _ptr(o_pre, "o_pre", bf, n),
+                                          _ptr(cache, "cache", torch.uint8), cache.numel(),
+                                          _stream(stream)), "qi_prefix_kv_build_noalloc")
 
 
 def qi_denoise_attn_step(plan, cache, q_img, k_img, v_img, o_img, stream=None):

@@ -132,6 +132,22 @@ qi_status qi_prefix_kv_build(qi_plan *plan, const void *q_pre, const void *k_pre
                              const void *v_pre, void *o_pre, void *d_cache,
                              size_t cache_bytes, void *stream);
 
+/* Allocation-free variant of qi_prefix_kv_build, for callers that cannot allocate device
+ * memory at the time of the call (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, results bit-identical to
+ * qi_prefix_kv_build.  The fp8 quantisation's per-chunk absmax partials, which the
+ * ordinary call keeps in the workspace, go to a static device array of the library
+ * (QI_NOALLOC_MAX_PARTIALS floats, 1 MiB, held by each GPU the library runs on until the
+ * process ends); the workspace must still have been uploaded (QI_ERR_STATE otherwise),
+ * since it holds the plan's tables.  Plans whose partials exceed the array
+ * (sum over requests of ceil(L_p / 64) * 2 * H floats) get QI_ERR_BUFFER_TOO_SMALL before
+ * anything is enqueued.  Calls on one GPU share the array: calls that overlap in time on
+ * one GPU (other streams, other threads) race and must not be made. */
+#define QI_NOALLOC_MAX_PARTIALS 262144
+qi_status qi_prefix_kv_build_noalloc(qi_plan *plan, const void *q_pre, const void *k_pre,
+                                     const void *v_pre, void *o_pre, void *d_cache,
+                                     size_t cache_bytes, void *stream);
+
 /* Denoising step: attention of the image rows over the cached prefix keys followed by the
  * live image keys of the same request -- the remaining steps reuse the cached prefix K/V
  * exactly and recompute only the image rows (vLLM recipe "Qwen/Qwen-Image-2.1", section

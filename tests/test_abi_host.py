@@ -207,3 +207,27 @@ def test_launch_schedule_covers_every_row_once(reqs, h, d):
     assert qi.lib.qi_plan_launch_items(p.handle, 1, None, 0, ctypes.byref(n)) == \
         qi.QI_ERR_BUFFER_TOO_SMALL
     assert n.value == 4 * len(qi.qi_plan_launch_items(p, 1))
+
+
+def test_noalloc_build_rejects_plans_beyond_its_scratch():
+    """qi_prefix_kv_build_noalloc refuses, before anything is enqueued, a plan whose fp8
+    absmax partials (sum of ceil(L_p / 64) * 2 * H floats) exceed its static array; the
+    ordinary build has no such limit (fake, never-touched device addresses)."""
+    A = ctypes.c_void_p(0x10000)
+    big = ctypes.c_size_t(1 << 40)
+    over = qi.Plan([[70000, 1]], 128, 64, "fp8")          # 1094 * 2 * 128 = 280064 floats
+    assert 1094 * 2 * 128 > qi.QI_NOALLOC_MAX_PARTIALS
+    assert qi.lib.qi_prefix_kv_build_noalloc(over.handle, A, A, A, A, A, big, None) == \
+        qi.QI_ERR_BUFFER_TOO_SMALL
+    # within the limit the next check (workspace never uploaded) answers instead
+    under = qi.Plan([[65000, 1]], 128, 64, "fp8")         # 1016 * 2 * 128 = 260096 floats
+    assert 1016 * 2 * 128 <= qi.QI_NOALLOC_MAX_PARTIALS
+    assert qi.lib.qi_prefix_kv_build_noalloc(under.handle, A, A, A, A, A, big, None) == \
+        qi.QI_ERR_STATE
+    assert qi.lib.qi_prefix_kv_build(over.handle, A, A, A, A, A, big, None) == qi.QI_ERR_STATE
+    assert qi.lib.qi_prefix_kv_build_noalloc(over.handle, None, A, A, A, A, big, None) == \
+        qi.QI_ERR_INVALID_ARG
+    # a bf16 cache has no partials
+    bf = qi.Plan([[70000, 1]], 128, 64, "bf16")
+    assert qi.lib.qi_prefix_kv_build_noalloc(bf.handle, A, A, A, A, A, big, None) == \
+        qi.QI_ERR_STATE
