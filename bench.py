@@ -55,7 +55,7 @@ class Layers:
         import dataclasses
         import torch
         from block_causal_attention_qi_amd import qi, synth
-        self.w = synth.WORKLOADS[name]
+        self.w = synth.workload(name)
         if kv is not None:
             self.w = dataclasses.replace(self.w, kv_dtype=kv)
         w = self.w
@@ -216,16 +216,20 @@ def measure(name, steps, warmup, layers, dev, with_full=False, with_build=True,
     oracle on that sample of the same inputs on the host, before the GPU work."""
     from block_causal_attention_qi_amd import qi, synth
     t0 = time.time()
-    x = synth.generate(synth.WORKLOADS[name], steps=1)
+    x = synth.generate(synth.workload(name), steps=1)
     log("[bench] %s: inputs drawn in %.1fs" % (name, time.time() - t0))
     cpu = oracle_time(name, x, *oracle_sample) if oracle_sample else None
     L = Layers(name, layers, dev, need_full=with_full, kv=kv, x=x)
     del x
     flops = qi.useful_flops(L.plan, qi.QI_CALL_DENOISE)
+    items = qi.qi_plan_launch_items(L.plan, qi.QI_CALL_DENOISE)
+    live = items[items[:, 0] >= 0]
     res = {"workload": name, "requests": L.w.requests, "heads": L.w.n_heads,
            "head_dim": L.w.head_dim, "kv_cache": L.w.kv_dtype, "layers": layers,
            "kernel": kernel_label(L.w.head_dim, L.w.kv_dtype),
-           "denoise_gflop_per_layer": flops / 1e9}
+           "denoise_gflop_per_layer": flops / 1e9,
+           "denoise_workgroups": int(len(live)),
+           "key_chunks": bool((live[:, 4] > 0).any())}
     if cpu:
         res["oracle_cpu"] = dict(cpu, tflops=flops / cpu["seconds_per_layer_step"] / 1e12)
     L.build()   # step 0 of every layer (untimed here: the caches must exist)
@@ -296,7 +300,7 @@ def oracle_time(name, x, heads=None, row_frac=1.0, min_seconds=0.0, max_reps=1):
     were made."""
     from block_causal_attention_qi_amd import synth
     from oracle import attention as A
-    w = synth.WORKLOADS[name]
+    w = synth.workload(name)
     nh = w.n_heads if heads is None else min(heads, w.n_heads)
     e = lambda a: synth.bf16_exact(a[:, :nh])
     args, rows = [], 0
@@ -333,7 +337,7 @@ def cpu_baseline(name, others):
     the other configurations (others: workload -> the oracle_cpu record of its measure)."""
     from block_causal_attention_qi_amd import synth
     from oracle import layout as OL
-    w = synth.WORKLOADS[name]
+    w = synth.workload(name)
     x = synth.generate(w, steps=1)
     rec = oracle_time(name, x, min_seconds=10.0, max_reps=8)
     del x
@@ -441,6 +445,11 @@ def main():
             extra[n] = measure(n, max(2, a.steps // 2), 1, a.layers, dev, with_full=(n == "edit4"),
                                oracle_sample=sample)
             log("[bench] %s" % json.dumps(extra[n]))
+        # one GPU's head shard (3 of 24 heads) of the edit workloads: the plan splits
+        # keys into chunks to fill the chip
+        for n in ("edit4@h3", "edit2048@h3"):
+            extra[n] = measure(n, max(2, a.steps // 2), 1, a.layers, dev, with_full=(n == "edit4@h3"))
+            log("[bench] %s" % json.dumps(extra[n]))
         if a.extra:
             # true CFG: both branches in one wave against the positive branch alone
             for n in ("edit1", "cfg_edit1"):
@@ -505,6 +514,10 @@ def main():
     if "wave8" in extra:
         summary["wave8_fp8_compulsory_gb_per_s"] = round(extra["wave8"]["compulsory_gb_per_s"], 1)
         summary["wave8_fp8_tflops"] = round(extra["wave8"]["tflops"], 1)
+    for n in ("edit4", "edit2048"):
+        if n + "@h3" in extra and n in extra:
+            summary[n + "_h3_tflops"] = round(extra[n + "@h3"]["tflops"], 1)
+            summary[n + "_h3_over_h24"] = round(extra[n + "@h3"]["tflops"] / extra[n]["tflops"], 3)
     if summary:
         out["north_star"] = summary
     clk = main_res.get("clock")

@@ -150,6 +150,7 @@ struct TileArgs {
   const __bf16 *k, *v;       // live K/V (token-major [tokens][H][D])
   const uint8_t *cache;      // prefix cache arena (denoise) or null
   int H, h, kend, kv_tok, lp;
+  int t0;                    // first key tile the workgroup visits (its key chunk)
   int64_t k_off, v_off;
   float k_scale, v_scale;    // fp8 dequantisation scales of this (request, head)
 };
@@ -345,6 +346,7 @@ __device__ __forceinline__ void sync_tile(int kt, const TileArgs &a, const __bf1
 // and conversion for tiles wholly in an E4M3FN cache tensor, the synchronous path for
 // mixed coded tiles.  Scales of coded tiles are folded in: K's into the logit scale (ck),
 // V's into P (vsc).
+// Tile indices m passed to the loader count from the workgroup's first key tile (a.t0).
 template <int D, int SRC, bool HALF>
 struct Loader {
   static constexpr bool CK = coded(SRC, 0), CV = coded(SRC, 1);
@@ -361,6 +363,7 @@ struct Loader {
   // before the loop: every tile straight into its ring slot
   template <bool IS_K>
   __device__ __forceinline__ void pro(int m, const TileArgs &a, __bf16 *slot, int hf = 0) {
+    m += a.t0;
     if constexpr (IS_K ? CK : CV)
       sync_tile<D, SRC, HALF, IS_K>(m, a, IS_K ? a.k : a.v, IS_K ? a.k_off : a.v_off, slot, hf);
     else
@@ -369,6 +372,7 @@ struct Loader {
   // in the loop: cached coded tiles land and are converted two periods later
   template <bool IS_K>
   __device__ __forceinline__ void issue(int m, const TileArgs &a, __bf16 *slot, int hf = 0) {
+    m += a.t0;
     if constexpr (IS_K ? CK : CV) {
       const int kd = tile_kind<SRC>(m, a);
       if (kd == CACHED) {
@@ -385,15 +389,16 @@ struct Loader {
   // convert tile m if it was landed (the caller knows it was issued two periods ago)
   template <bool IS_K>
   __device__ __forceinline__ void convert(int m, const TileArgs &a, __bf16 *slot, int hf = 0) const {
+    m += a.t0;
     if constexpr (IS_K ? CK : CV)
       if (tile_kind<SRC>(m, a) == CACHED) cm.template convert<IS_K>(IS_K ? lk : lv, slot, hf);
   }
   __device__ __forceinline__ float ck(int m, const TileArgs &a, float c) const {
-    if constexpr (CK) return tile_kind<SRC>(m, a) == CACHED ? c * a.k_scale : c;
+    if constexpr (CK) return tile_kind<SRC>(m + a.t0, a) == CACHED ? c * a.k_scale : c;
     return c;
   }
   __device__ __forceinline__ bool vsc(int m, const TileArgs &a) const {
-    if constexpr (CV) return tile_kind<SRC>(m, a) == CACHED;
+    if constexpr (CV) return tile_kind<SRC>(m + a.t0, a) == CACHED;
     return false;
   }
 };
@@ -662,6 +667,31 @@ __device__ __forceinline__ void store_o_lds(__bf16 *o, const qi_tile &tl, int H,
   }
 }
 
+// A key chunk's unnormalised state of the wavefront's 32 rows (row0 .. row0 + 31 of the
+// tile) into partial slot tl.part + h: O as fp32 [row][D] (lane (j, g) writes 16 bytes
+// per 8 dims: dims 32 db + 8 aa + 4 g .. + 3 of row j), then m and l per row.
+template <int D>
+__device__ __forceinline__ void store_part(float *part, const qi_tile &tl, int h, int row0,
+                                           const f32x16_t (&acc)[Cfg<D>::DB], float m_run,
+                                           float l_run) {
+  using C = Cfg<D>;
+  const int lane = threadIdx.x & 63;
+  const int j = lane & 31, g = lane >> 5;
+  float *slot = part + (size_t)(tl.part + h) * QI_PART_SLOT_FLOATS(D);
+  float *orow = slot + (size_t)(row0 + j) * D + 4 * g;
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int aa = 0; aa < 4; ++aa)
+      *reinterpret_cast<float4 *>(orow + 32 * db + 8 * aa) =
+          make_float4(acc[db][4 * aa], acc[db][4 * aa + 1], acc[db][4 * aa + 2], acc[db][4 * aa + 3]);
+  const float l = pair_sum(l_run);
+  if (g == 0) {
+    slot[(size_t)QI_ROWS * D + row0 + j] = m_run;
+    slot[(size_t)QI_ROWS * D + QI_ROWS + row0 + j] = l;
+  }
+}
+
 __device__ __forceinline__ TileArgs make_args(const qi_tile &tl, int H, int h, const __bf16 *k,
                                               const __bf16 *v, const uint8_t *cache, bool fp8) {
   TileArgs a;
@@ -671,6 +701,7 @@ __device__ __forceinline__ TileArgs make_args(const qi_tile &tl, int H, int h, c
   a.H = H;
   a.h = h;
   a.kend = tl.kend;
+  a.t0 = tl.k0 / BN;
   a.kv_tok = tl.kv_tok;
   a.lp = tl.lp;
   a.k_off = tl.k_off;
@@ -743,13 +774,13 @@ __device__ __forceinline__ __bf16 *q_stage(const Ring &r) {
 template <int D, int SRC>
 __device__ __forceinline__ void pp_rows256(const Ring &r, const qi_tile &tl, int H, int h,
                                            const TileArgs &a, const __bf16 *q, __bf16 *o,
-                                           float c) {
+                                           float *part, float c) {
   using C = Cfg<D>;
   const int wave = threadIdx.x >> 6;
   const int group = wave >> 2;
   const bool active = wave * 32 < tl.nrows;   // the wavefront's rows exist
 
-  const int n = (tl.kend + BN - 1) / BN;
+  const int n = (tl.k1 - tl.k0 + BN - 1) / BN;   // key tiles of the chunk
   constexpr bool FP8 = SRC == SRC_CACHE_FP8 || SRC == SRC_CACHE_FP8V;
   Loader<D, SRC, true> ld;
   ld.init(a, r.LK, r.LV);
@@ -795,7 +826,7 @@ __device__ __forceinline__ void pp_rows256(const Ring &r, const qi_tile &tl, int
     } else {
       if (active && t >= 1 && t <= n) {
         raise_max<D>(acc, m_run, l_run, mc);
-        if (t * BN > tl.kend) mask_tile(s, t - 1, tl.kend);   // tile t - 1 is PARTIAL
+        if ((a.t0 + t) * BN > tl.kend) mask_tile(s, a.t0 + t - 1, tl.kend);   // PARTIAL
         tile_exp<FP8>(s, m_run, ld.ck(t - 1, a, c), ld.vsc(t - 1, a), log2_vs, inv_vs, l_run, p);
       }
       __builtin_amdgcn_s_waitcnt(0);
@@ -813,7 +844,7 @@ __device__ __forceinline__ void pp_rows256(const Ring &r, const qi_tile &tl, int
     } else {
       if (active && t < n) {
         raise_max<D>(acc, m_run, l_run, mc);
-        if ((t + 1) * BN > tl.kend) mask_tile(s, t, tl.kend);   // tile t is PARTIAL
+        if ((a.t0 + t + 1) * BN > tl.kend) mask_tile(s, a.t0 + t, tl.kend);   // PARTIAL
         tile_exp<FP8>(s, m_run, ld.ck(t, a, c), ld.vsc(t, a), log2_vs, inv_vs, l_run, p);
       }
       __builtin_amdgcn_s_waitcnt(0);
@@ -836,9 +867,13 @@ __device__ __forceinline__ void pp_rows256(const Ring &r, const qi_tile &tl, int
   }
   // the ring is free: every load was waited for and every read consumed before the last
   // barrier; wavefront w stages its rows in half w & 1 of K slot w >> 1
-  if (active)
-    store_o_lds<D>(o, tl, H, h, wave * 32, acc, l_run,
-                   ring_k(r, wave >> 1) + (wave & 1) * 32 * D);
+  if (active) {
+    if (tl.part >= 0)
+      store_part<D>(part, tl, h, wave * 32, acc, m_run, l_run);
+    else
+      store_o_lds<D>(o, tl, H, h, wave * 32, acc, l_run,
+                     ring_k(r, wave >> 1) + (wave & 1) * 32 * D);
+  }
 }
 
 // Row tiles of at most 128 rows: wavefronts w and w+4 hold the same 32 rows and the two
@@ -855,13 +890,13 @@ __device__ __forceinline__ void pp_rows256(const Ring &r, const qi_tile &tl, int
 template <int D, int SRC>
 __device__ __forceinline__ void pp_rows128(const Ring &r, const qi_tile &tl, int H, int h,
                                            const TileArgs &a, const __bf16 *q, __bf16 *o,
-                                           float c) {
+                                           float *part, float c) {
   using C = Cfg<D>;
   const int wave = threadIdx.x >> 6;
   const int group = wave >> 2;
   const bool active = (wave & 3) * 32 < tl.nrows;   // the wavefront's rows exist
 
-  const int n = (tl.kend + BN - 1) / BN;
+  const int n = (tl.k1 - tl.k0 + BN - 1) / BN;   // key tiles of the chunk
   constexpr bool FP8 = SRC == SRC_CACHE_FP8 || SRC == SRC_CACHE_FP8V;
   Loader<D, SRC, false> ld;   // whole tiles; coded ones land in the group's region
   ld.init(a, r.LK, r.LV);
@@ -901,7 +936,7 @@ __device__ __forceinline__ void pp_rows128(const Ring &r, const qi_tile &tl, int
     } else {
       if (active && per >= 1 && per <= n) {
         raise_max<D>(acc, m_run, l_run, mc);
-        if (per * BN > tl.kend) mask_tile(s, per - 1, tl.kend);   // tile per - 1 is PARTIAL
+        if ((a.t0 + per) * BN > tl.kend) mask_tile(s, a.t0 + per - 1, tl.kend);   // PARTIAL
         tile_exp<FP8>(s, m_run, ld.ck(per - 1, a, c), ld.vsc(per - 1, a), log2_vs, inv_vs, l_run, p);
       }
       __builtin_amdgcn_s_waitcnt(0);   // this group's loads of two periods ago
@@ -945,8 +980,10 @@ __device__ __forceinline__ void pp_rows128(const Ring &r, const qi_tile &tl, int
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) acc[db][rr] = acc[db][rr] * a0 + ost[(16 * db + rr) * 64] * a1;
     l_run = l_run * a0 + l1 * a1;
-    // stage in this wavefront's own merge buffer, whose values are now in registers
-    store_o_lds<D>(o, tl, H, h, w4 * 32, acc, l_run, ring_k(r, w4));
+    if (tl.part >= 0)
+      store_part<D>(part, tl, h, w4 * 32, acc, mm, l_run);
+    else   // stage in this wavefront's own merge buffer, whose values are now in registers
+      store_o_lds<D>(o, tl, H, h, w4 * 32, acc, l_run, ring_k(r, w4));
   }
 }
 
@@ -954,7 +991,8 @@ template <int D, int SRC>
 __global__ __launch_bounds__(NT, 1) void attn_pp_kernel(
     const int32_t *__restrict__ sched, const qi_tile *__restrict__ tiles, int H,
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
-    __bf16 *__restrict__ o, const uint8_t *__restrict__ cache, float c) {
+    __bf16 *__restrict__ o, const uint8_t *__restrict__ cache, float *__restrict__ part,
+    float c) {
   using C = Cfg<D>;
   __shared__ __attribute__((aligned(1024))) __bf16 K0[C::KTILE], K1[C::KTILE], K2[C::KTILE], K3[C::KTILE];
   __shared__ __attribute__((aligned(1024))) __bf16 V0[C::VTILE], V1[C::VTILE], V2[C::VTILE], V3[C::VTILE];
@@ -975,11 +1013,49 @@ __global__ __launch_bounds__(NT, 1) void attn_pp_kernel(
   const TileArgs a = make_args(tl, H, h, k, v, cache, SRC == SRC_CACHE_FP8 || SRC == SRC_CACHE_FP8V);
   const Ring r{K0, K1, K2, K3, V0, V1, V2, V3, lk, lv};
   if (tl.nrows > 128)
-    pp_rows256<D, SRC>(r, tl, H, h, a, q, o, c);
+    pp_rows256<D, SRC>(r, tl, H, h, a, q, o, part, c);
   else
-    pp_rows128<D, SRC>(r, tl, H, h, a, q, o, c);
+    pp_rows128<D, SRC>(r, tl, H, h, a, q, o, part, c);
 }
 #undef QI_RING
+
+// Merge of key chunks: row (tile, head) gets O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M)
+// l_s over its chunks s in chunk order (M = max_s m_s), rounded to bf16 -- the same
+// combination the online softmax applies between key tiles, done once per chunk.  A
+// thread owns 4 dims of one row; a block covers RPB rows of one (tile, head).
+template <int D>
+__global__ __launch_bounds__(256) void merge_chunks(const qi_merge *__restrict__ mg, int H,
+                                                    const float *__restrict__ part,
+                                                    __bf16 *__restrict__ o) {
+  constexpr int TPR = D / 4, RPB = 256 / TPR, BPT = QI_ROWS / RPB;
+  const int b = blockIdx.x;
+  const int e = b / (H * BPT), h = (b / BPT) % H, rb = b % BPT;
+  const qi_merge m = mg[e];
+  const int row = rb * RPB + (int)threadIdx.x / TPR;
+  if (row >= m.nrows) return;
+  const int d = ((int)threadIdx.x % TPR) * 4;
+  const size_t SLOT = QI_PART_SLOT_FLOATS(D), MO = (size_t)QI_ROWS * D;
+  float mx = -INFINITY;
+  for (int s = 0; s < m.nchunks; ++s)
+    mx = fmaxf(mx, part[(size_t)(m.part0 + s * H + h) * SLOT + MO + row]);
+  float l = 0.0f;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int s = 0; s < m.nchunks; ++s) {
+    const float *sl = part + (size_t)(m.part0 + s * H + h) * SLOT;
+    const float w = __builtin_amdgcn_exp2f(sl[MO + row] - mx);
+    l = __builtin_fmaf(w, sl[MO + QI_ROWS + row], l);
+    const float4 v = *reinterpret_cast<const float4 *>(sl + (size_t)row * D + d);
+    acc.x = __builtin_fmaf(w, v.x, acc.x);
+    acc.y = __builtin_fmaf(w, v.y, acc.y);
+    acc.z = __builtin_fmaf(w, v.z, acc.z);
+    acc.w = __builtin_fmaf(w, v.w, acc.w);
+  }
+  const float inv = 1.0f / l;
+  uint2 u;
+  u.x = pack_bf16(acc.x * inv, acc.y * inv);
+  u.y = pack_bf16(acc.z * inv, acc.w * inv);
+  *reinterpret_cast<uint2 *>(o + ((int64_t)(m.q_tok + row) * H + h) * D + d) = u;
+}
 
 template <int D, int SRC>
 qi_status launch(const qi_plan *p, int call, const void *q, const void *k, const void *v,
@@ -988,13 +1064,22 @@ qi_status launch(const qi_plan *p, int call, const void *q, const void *k, const
   const float c = (float)(1.4426950408889634 / std::sqrt((double)D));   // log2(e)/sqrt(D)
   const auto kern = attn_pp_kernel<D, SRC>;
   const int nt = NT;
+  float *part = reinterpret_cast<float *>(const_cast<uint8_t *>(ws) + p->kpart_off);
   hipLaunchKernelGGL(kern, dim3(p->sched_len[call]), dim3(nt), 0, s,
                      reinterpret_cast<const int32_t *>(ws + p->sched_off[call]),
                      reinterpret_cast<const qi_tile *>(ws + p->tiles_off[call]), p->H,
                      static_cast<const __bf16 *>(q), static_cast<const __bf16 *>(k),
                      static_cast<const __bf16 *>(v), static_cast<__bf16 *>(o),
-                     static_cast<const uint8_t *>(cache), c);
-  return hipGetLastError() == hipSuccess ? QI_OK : QI_ERR_HIP;
+                     static_cast<const uint8_t *>(cache), part, c);
+  if (hipGetLastError() != hipSuccess) return QI_ERR_HIP;
+  if (p->n_merge[call] > 0) {
+    constexpr int BPT = QI_ROWS / (256 / (D / 4));   // blocks per (tile, head)
+    hipLaunchKernelGGL(merge_chunks<D>, dim3(p->n_merge[call] * p->H * BPT), dim3(256), 0, s,
+                       reinterpret_cast<const qi_merge *>(ws + p->merge_off[call]), p->H,
+                       static_cast<const float *>(part), static_cast<__bf16 *>(o));
+    if (hipGetLastError() != hipSuccess) return QI_ERR_HIP;
+  }
+  return QI_OK;
 }
 
 }  // namespace

@@ -9,6 +9,8 @@
 // section "Online serving").
 #include <algorithm>
 #include <cmath>
+#include <map>
+#include <tuple>
 #include <cstring>
 #include <new>
 #include <numeric>
@@ -53,7 +55,7 @@ struct Unit {           // all row tiles of one (request, head): they read the s
 
 // Cost of one (row tile, head) item: key tiles visited x 128-row blocks.
 int64_t item_cost(const qi_tile &t) {
-  return (int64_t)((t.kend + QI_KERNEL_BN - 1) / QI_KERNEL_BN) * ((t.nrows + 127) / 128);
+  return (int64_t)((t.k1 - t.k0 + QI_KERNEL_BN - 1) / QI_KERNEL_BN) * ((t.nrows + 127) / 128);
 }
 
 // Deal the (tile, head) items of a call to the XCDs and order them for launch.
@@ -70,15 +72,22 @@ void build_schedule(const qi_plan &p, std::vector<qi_tile> &tiles,
                     const std::vector<std::pair<int, int>> &items_in, int slots_per_xcd,
                     bool may_split, std::vector<int32_t> &sched) {
   std::vector<Unit> units;
-  std::vector<int> unit_of(p.n_req * p.H, -1);
+  std::map<std::tuple<int, int, int, int>, int> unit_of;
+  std::map<std::tuple<int, int, int>, int> run_len;
   for (auto [t, h] : items_in) {
-    int &u = unit_of[tiles[t].req * p.H + h];
-    if (u < 0) {
-      u = (int)units.size();
+    // a unit shares one stream of K/V: (request, head), or with key chunks (request,
+    // head, chunk) cut into runs of at most 8 row tiles -- a head shard has too few
+    // (request, head) pairs to spread over the XCDs
+    int run = 0;
+    if (p.kchunk_tiles > 0) run = run_len[{tiles[t].req, h, tiles[t].k0}]++ / 8;
+    const auto key = std::make_tuple(tiles[t].req, h, p.kchunk_tiles > 0 ? tiles[t].k0 : 0, run);
+    auto it = unit_of.find(key);
+    if (it == unit_of.end()) {
+      it = unit_of.emplace(key, (int)units.size()).first;
       units.push_back(Unit{tiles[t].req, h, 0, {}});
     }
-    units[u].tiles.push_back(t);
-    units[u].cost += item_cost(tiles[t]);
+    units[it->second].tiles.push_back(t);
+    units[it->second].cost += item_cost(tiles[t]);
   }
   for (Unit &u : units)
     std::stable_sort(u.tiles.begin(), u.tiles.end(), [&](int a, int b) {
@@ -163,6 +172,9 @@ void build_tiles(const qi_plan &p, int call, std::vector<qi_tile> &tiles) {
         qi_tile t{};
         t.nrows = std::min(bm, start + len - r0);
         t.kend = std::min(visible_end(rq, r0), nkeys);
+        t.k0 = 0;
+        t.k1 = t.kend;
+        t.part = -1;
         t.req = r;
         t.k_off = rq.k_off;
         t.v_off = rq.v_off;
@@ -184,6 +196,80 @@ void build_tiles(const qi_plan &p, int call, std::vector<qi_tile> &tiles) {
       }
     }
   }
+}
+
+// Key tiles a row tile visits without a key split.
+int key_tiles(const qi_tile &t) { return (t.kend + QI_KERNEL_BN - 1) / QI_KERNEL_BN; }
+
+// Key split.  When the denoising call has fewer (row tile, head) items than compute units
+// (a head-sharded deployment: three heads of 24 per GPU), much of the chip would idle, so
+// every row tile's keys are cut into chunks of ct key tiles, each its own workgroup, and
+// the chunks' partial softmax states are merged afterwards.  ct minimises an estimate of
+// the call's time in key-tile units: rounds of one workgroup per CU times (the longest
+// chunk plus a workgroup's fixed cost), plus the merge's traffic per partial slot; the
+// split is taken only when that beats the whole row tiles by more than 5%.  0: no split.
+// One ct per plan: every call cuts a given row tile at the same keys, so reuse stays
+// bit-identical.
+constexpr double kWgFixedTiles = 2.0;     // prologue (Q and first tiles) and epilogue
+constexpr double kMergeSlotTiles = 0.03;  // a slot's partial state written and read back
+double split_cost(const std::vector<qi_tile> &den, int H, int ct) {
+  int64_t wgs = 0;
+  int longest = 0;
+  for (const qi_tile &t : den) {
+    const int n = key_tiles(t);
+    wgs += (int64_t)H * (ct > 0 ? (n + ct - 1) / ct : 1);
+    longest = std::max(longest, ct > 0 ? std::min(ct, n) : n);
+  }
+  const double rounds = (double)((wgs + QI_NUM_CUS - 1) / QI_NUM_CUS);
+  return rounds * (longest + kWgFixedTiles) + (ct > 0 ? wgs * kMergeSlotTiles : 0.0);
+}
+int choose_chunk_tiles(const std::vector<qi_tile> &den, int H) {
+  if (den.empty() || (int64_t)den.size() * H >= QI_NUM_CUS) return 0;
+  int max_t = 0;
+  for (const qi_tile &t : den) max_t = std::max(max_t, key_tiles(t));
+  int best = 0;
+  double best_cost = 0.95 * split_cost(den, H, 0);
+  for (int ct = QI_SPLIT_MIN_TILES; ct < max_t; ++ct) {
+    const double c = split_cost(den, H, ct);
+    if (c < best_cost) {
+      best_cost = c;
+      best = ct;
+    }
+  }
+  return best;
+}
+
+// Cut the row tiles of one call into key chunks of ct tiles: a row tile of more than ct
+// key tiles becomes nchunks tiles (chunk s: keys [s ct BN, min((s+1) ct BN, kend)),
+// partial slots part0 + s H + head) and one merge entry; the others stay whole.  Partial
+// slots are numbered from 0 per call.
+void split_keys(int ct, int H, std::vector<qi_tile> &tiles, std::vector<qi_merge> &merges,
+                std::vector<int> &merge_req, int64_t &slots) {
+  merges.clear();
+  merge_req.clear();
+  slots = 0;
+  if (ct <= 0) return;
+  std::vector<qi_tile> out;
+  for (const qi_tile &t : tiles) {
+    const int nt = key_tiles(t);
+    if (nt <= ct) {
+      out.push_back(t);
+      continue;
+    }
+    const int nch = (nt + ct - 1) / ct;
+    merges.push_back(qi_merge{t.q_tok, t.nrows, nch, (int32_t)slots});
+    merge_req.push_back(t.req);
+    for (int c = 0; c < nch; ++c) {
+      qi_tile u = t;
+      u.k0 = c * ct * QI_KERNEL_BN;
+      u.k1 = std::min((c + 1) * ct * QI_KERNEL_BN, t.kend);
+      u.part = (int32_t)(slots + (int64_t)c * H);
+      u.pad = c;   // chunk index (host bookkeeping)
+      out.push_back(u);
+    }
+    slots += (int64_t)nch * H;
+  }
+  tiles.swap(out);
 }
 
 template <typename T>
@@ -296,6 +382,9 @@ qi_status qi_plan_create(const qi_wave_desc *d, qi_plan **out) {
   }
   std::vector<qi_tile> tiles[3];
   std::vector<int32_t> sched[3];
+  std::vector<qi_merge> merges[3];
+  std::vector<int> merge_req[3];
+  int64_t slots[3] = {0, 0, 0};
   // prefix and denoising calls: row tiles per block, balanced (and split) per call.  The
   // full call reuses exactly their decomposition, (row tile, head) by (row tile, head),
   // so every row runs the same kernel path over the same key tiles in every call and the
@@ -303,17 +392,37 @@ qi_status qi_plan_create(const qi_wave_desc *d, qi_plan **out) {
   for (int c : {QI_CALL_PREFIX, QI_CALL_DENOISE}) {
     p->bm[c] = QI_ROWS;
     build_tiles(*p, c, tiles[c]);
+  }
+  p->kchunk_tiles = choose_chunk_tiles(tiles[QI_CALL_DENOISE], p->H);
+  for (int c : {QI_CALL_PREFIX, QI_CALL_DENOISE}) {
+    split_keys(p->kchunk_tiles, p->H, tiles[c], merges[c], merge_req[c], slots[c]);
     std::vector<std::pair<int, int>> items;
     for (int t = 0; t < (int)tiles[c].size(); ++t)
       for (int h = 0; h < p->H; ++h) items.push_back({t, h});
-    // the kernel runs one 8-wavefront workgroup per CU
-    build_schedule(*p, tiles[c], items, QI_CUS_PER_XCD, true, sched[c]);
+    // the kernel runs one 8-wavefront workgroup per CU; key-split plans keep row tiles
+    // whole (their chunks already fill the chip)
+    build_schedule(*p, tiles[c], items, QI_CUS_PER_XCD, p->kchunk_tiles == 0, sched[c]);
   }
   {
     p->bm[QI_CALL_FULL] = QI_ROWS;
     std::vector<std::pair<int, int>> items;
     std::vector<qi_tile> &ft = tiles[QI_CALL_FULL];
     for (int c : {QI_CALL_PREFIX, QI_CALL_DENOISE}) {
+      // the source call's merge groups get slots of their own in the full call
+      std::vector<int64_t> base_of(merges[c].size());
+      std::vector<int> group_of_part;   // source slot base -> merge group
+      for (size_t m = 0; m < merges[c].size(); ++m) {
+        const qi_merge &e = merges[c][m];
+        const qi_req_host &rq = p->req[merge_req[c][m]];
+        const int r0 = c == QI_CALL_PREFIX ? e.q_tok - rq.pre_tok : e.q_tok - rq.img_tok + rq.lp;
+        base_of[m] = slots[QI_CALL_FULL];
+        merges[QI_CALL_FULL].push_back(
+            qi_merge{rq.all_tok + r0, e.nrows, e.nchunks, (int32_t)slots[QI_CALL_FULL]});
+        merge_req[QI_CALL_FULL].push_back(merge_req[c][m]);
+        slots[QI_CALL_FULL] += (int64_t)e.nchunks * p->H;
+        if ((int)group_of_part.size() <= e.part0) group_of_part.resize(e.part0 + 1, -1);
+        group_of_part[e.part0] = (int)m;
+      }
       std::vector<int> map(tiles[c].size(), -1);
       for (int32_t code : sched[c]) {
         if (code < 0) continue;
@@ -327,6 +436,10 @@ qi_status qi_plan_create(const qi_wave_desc *d, qi_plan **out) {
           f.q_tok = rq.all_tok + r0;
           f.kv_tok = rq.all_tok;
           f.lp = 0;
+          if (src.part >= 0) {
+            const int g = group_of_part[src.part - src.pad * p->H];
+            f.part = (int32_t)(base_of[g] + (int64_t)src.pad * p->H);
+          }
           map[t] = (int)ft.size();
           ft.push_back(f);
         }
@@ -335,6 +448,7 @@ qi_status qi_plan_create(const qi_wave_desc *d, qi_plan **out) {
     }
     build_schedule(*p, ft, items, QI_CUS_PER_XCD, false, sched[QI_CALL_FULL]);
   }
+  p->kpart_slots = std::max({slots[0], slots[1], slots[2]});
   size_t off = 0;
   p->reqs_off = off;
   off = align_up(off + reqs.size() * sizeof(qi_req_dev));
@@ -345,16 +459,22 @@ qi_status qi_plan_create(const qi_wave_desc *d, qi_plan **out) {
     off = align_up(off + tiles[c].size() * sizeof(qi_tile));
     p->sched_off[c] = off;
     off = align_up(off + sched[c].size() * sizeof(int32_t));
+    p->n_merge[c] = (int32_t)merges[c].size();
+    p->merge_off[c] = off;
+    off = align_up(off + merges[c].size() * sizeof(qi_merge));
   }
   p->part_off = off;
   p->part_floats = p->kv != QI_KV_BF16 ? nparts : 0;
   off = align_up(off + p->part_floats * sizeof(float));
+  p->kpart_off = off;
+  off = align_up(off + (size_t)p->kpart_slots * QI_PART_SLOT_FLOATS(p->D) * sizeof(float));
   p->ws_bytes = off;
   p->ws_image.assign(p->part_off, 0);
   put(p->ws_image, p->reqs_off, reqs);
   for (int c = 0; c < 3; ++c) {
     put(p->ws_image, p->tiles_off[c], tiles[c]);
     put(p->ws_image, p->sched_off[c], sched[c]);
+    put(p->ws_image, p->merge_off[c], merges[c]);
   }
   *out = p;
   return QI_OK;
@@ -412,15 +532,15 @@ qi_status qi_plan_launch_items(const qi_plan *p, int32_t call, int32_t *host_out
                                size_t *n_needed) {
   if (!p || call < 0 || call > 2) return QI_ERR_INVALID_ARG;
   const size_t len = (size_t)p->sched_len[call];
-  if (n_needed) *n_needed = 4 * len;
-  if (!host_out || n < 4 * len) return QI_ERR_BUFFER_TOO_SMALL;
+  if (n_needed) *n_needed = QI_LAUNCH_ITEM_FIELDS * len;
+  if (!host_out || n < QI_LAUNCH_ITEM_FIELDS * len) return QI_ERR_BUFFER_TOO_SMALL;
   const int32_t *sched = reinterpret_cast<const int32_t *>(p->ws_image.data() + p->sched_off[call]);
   const qi_tile *tiles = reinterpret_cast<const qi_tile *>(p->ws_image.data() + p->tiles_off[call]);
   for (size_t i = 0; i < len; ++i) {
-    int32_t *e = host_out + 4 * i;
+    int32_t *e = host_out + QI_LAUNCH_ITEM_FIELDS * i;
     const int32_t code = sched[i];
     if (code < 0) {
-      e[0] = e[1] = e[2] = e[3] = -1;
+      for (int f = 0; f < QI_LAUNCH_ITEM_FIELDS; ++f) e[f] = -1;
       continue;
     }
     const qi_tile &t = tiles[code / p->H];
@@ -431,6 +551,8 @@ qi_status qi_plan_launch_items(const qi_plan *p, int32_t call, int32_t *host_out
     e[1] = code % p->H;
     e[2] = t.q_tok - base;
     e[3] = t.nrows;
+    e[4] = t.k0;
+    e[5] = t.k1;
   }
   return QI_OK;
 }

@@ -21,7 +21,10 @@
 // Prefix tokens per workgroup in the cache-write kernels.
 #define QI_CACHE_CHUNK 64
 
-// One row tile of one request for one call (device table entry, 48 bytes).
+// One row tile of one request for one call, or one key chunk of it (device table entry,
+// 64 bytes).  The rows see keys [0, kend); the workgroup visits keys [k0, k1) of them:
+// [0, kend) unless the plan splits keys, then one chunk whose partial softmax state goes
+// to partial slot part + head and is merged afterwards.
 struct qi_tile {
   int32_t q_tok;      // packed token index (in the call's Q and O tensors) of the first row
   int32_t nrows;      // 1 .. row tile size of the call
@@ -32,8 +35,29 @@ struct qi_tile {
   int64_t k_off;      // byte offset of the request's cached K  [H][lp][D]   (denoise)
   int64_t v_off;      // byte offset of the request's cached V  [H][lp][D]   (denoise)
   int64_t s_off;      // byte offset of the request's scales [2][H] float32 (fp8 denoise)
+  int32_t k0, k1;     // visited keys [k0, k1): k0 a multiple of QI_KERNEL_BN, k1 <= kend
+  int32_t part;       // first partial slot of the chunk (slot part + head), or -1: store O
+  int32_t pad;
 };
-static_assert(sizeof(qi_tile) == 48, "qi_tile is a 48-byte device record");
+static_assert(sizeof(qi_tile) == 64, "qi_tile is a 64-byte device record");
+
+// One row tile whose keys were split into chunks, for the merge kernel (16 bytes): its
+// chunk s of head h left its state in partial slot part0 + s * H + h.
+struct qi_merge {
+  int32_t q_tok;      // packed token index of the first row (in the call's O)
+  int32_t nrows;
+  int32_t nchunks;
+  int32_t part0;
+};
+static_assert(sizeof(qi_merge) == 16, "qi_merge is a 16-byte device record");
+
+// Partial slot of a key chunk: the unnormalised O of up to QI_ROWS rows ([row][D] fp32),
+// then the rows' running max m (log2 units) and sum l: (QI_ROWS * D + 2 * QI_ROWS) floats.
+#define QI_PART_SLOT_FLOATS(D) ((size_t)QI_ROWS * (D) + 2 * QI_ROWS)
+// Key chunks are used only when the denoising call has fewer (row tile, head) items than
+// compute units; a chunk holds at least this many key tiles.
+#define QI_SPLIT_MIN_TILES 8
+#define QI_NUM_CUS (QI_NUM_XCD * QI_CUS_PER_XCD)
 
 // Per-request record for the cache-write kernels (device table entry, 48 bytes).
 struct qi_req_dev {
@@ -69,6 +93,13 @@ struct qi_plan {
   int32_t bm[3] = {0, 0, 0};   // row tile size per call
   size_t reqs_off = 0, part_off = 0, part_floats = 0;
   int32_t max_chunks = 0;
+  // key split: chunk length in key tiles (0: none), merge tables per call, and the
+  // partial slots (shared by the calls, which run one after the other on a plan)
+  int32_t kchunk_tiles = 0;
+  size_t merge_off[3] = {0, 0, 0};
+  int32_t n_merge[3] = {0, 0, 0};
+  size_t kpart_off = 0;
+  int64_t kpart_slots = 0;
 
   void *d_ws = nullptr;   // caller's workspace once uploaded
   bool built = false;     // a prefix build has been enqueued on this plan

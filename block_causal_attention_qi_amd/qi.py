@@ -21,6 +21,7 @@ QI_KV_BF16, QI_KV_FP8_E4M3, QI_KV_FP8_V = 0, 1, 2
 QI_CALL_PREFIX, QI_CALL_DENOISE, QI_CALL_FULL = 0, 1, 2
 QI_MAX_REQUESTS, QI_MAX_REFS, QI_MAX_HEADS = 64, 10, 128
 QI_NOALLOC_MAX_PARTIALS = 262144
+QI_LAUNCH_ITEM_FIELDS = 6
 
 EXPORTS = ("qi_plan_create", "qi_plan_destroy", "qi_plan_sizes", "qi_plan_upload",
            "qi_prefix_kv_build", "qi_prefix_kv_build_noalloc", "qi_denoise_attn_step", "qi_attn_full_reference_step",
@@ -253,16 +254,17 @@ def qi_plan_kernel_tile(plan, call):
 
 
 def qi_plan_launch_items(plan, call):
-    """Launch schedule of a call: int32 array [workgroups, 4] of (request, head, first
-    row as a position in the request's sequence, row count); padding rows are -1."""
+    """Launch schedule of a call: int32 array [workgroups, 6] of (request, head, first
+    row as a position in the request's sequence, row count, first key, end key: the key
+    chunk the workgroup visits); padding rows are -1."""
     need = ctypes.c_size_t()
     st = lib.qi_plan_launch_items(plan.handle, call, None, 0, ctypes.byref(need))
     if st not in (QI_OK, QI_ERR_BUFFER_TOO_SMALL):
         _check(st, "qi_plan_launch_items")
-    out = np.zeros(max(4, need.value), dtype=np.int32)
+    out = np.zeros(max(QI_LAUNCH_ITEM_FIELDS, need.value), dtype=np.int32)
     _check(lib.qi_plan_launch_items(plan.handle, call, out.ctypes.data_as(ctypes.c_void_p),
                                     out.size, ctypes.byref(need)), "qi_plan_launch_items")
-    return out[:need.value].reshape(-1, 4)
+    return out[:need.value].reshape(-1, QI_LAUNCH_ITEM_FIELDS)
 
 
 def qi_plan_cache_offset(plan, req, kv, head, tok):

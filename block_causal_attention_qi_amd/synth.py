@@ -126,9 +126,28 @@ class WaveInputs:
         return outs
 
 
+def head_shard(workload, heads=3, requests=None):
+    """One GPU's share of a workload under head (tensor or Ulysses) parallelism: the same
+    blocks with `heads` of its heads (3 of 24 on eight GPUs; vLLM recipe
+    "Qwen/Qwen-Image-2.1", section "Overview"), optionally only some of its requests
+    (indices).  Named "<name>@h<heads>"; drawn with the workload's seed."""
+    import dataclasses
+    w = WORKLOADS[workload] if isinstance(workload, str) else workload
+    reqs = w.requests if requests is None else [w.requests[i] for i in requests]
+    tag = "" if requests is None else "r" + "-".join(map(str, requests))
+    return dataclasses.replace(w, name="%s@h%d%s" % (w.name, heads, tag), n_heads=heads,
+                               requests=[list(b) for b in reqs])
+
+
+def workload(name):
+    """A workload by name: a key of WORKLOADS, or "<key>@h<n>" for its n-head shard."""
+    base, _, heads = name.partition("@h")
+    return head_shard(base, int(heads)) if heads else WORKLOADS[base]
+
+
 def generate(workload, steps=1, seed=None):
     """Draw a wave's inputs for `steps` denoising steps (see module docstring)."""
-    w = WORKLOADS[workload] if isinstance(workload, str) else workload
+    w = globals()["workload"](workload) if isinstance(workload, str) else workload
     rng = np.random.default_rng(w.seed if seed is None else seed)
     gam = [rng.uniform(0.8, 1.2, (w.n_heads, w.head_dim)).astype(np.float32)
            for _ in range(3)]

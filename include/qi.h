@@ -110,12 +110,16 @@ qi_status qi_plan_create(const qi_wave_desc *desc, qi_plan **out);
 void qi_plan_destroy(qi_plan *plan);
 
 /* Bytes the caller must provide: the cache arena of one layer, and the device workspace
- * (launch schedules plus fp8 absmax partials).  Either output pointer may be NULL. */
+ * (launch schedules, fp8 absmax partials, and the partial softmax states of key chunks
+ * when the plan splits keys -- see qi_plan_kernel_tile).  Either output pointer may be
+ * NULL. */
 qi_status qi_plan_sizes(const qi_plan *plan, size_t *cache_bytes, size_t *workspace_bytes);
 
 /* Copy the plan's schedules into the caller's device workspace (enqueued on stream) and
  * remember the workspace for the later calls.  The workspace must stay allocated and
- * untouched by the caller while the plan is in use.  May be called again to move it. */
+ * untouched by the caller while the plan is in use.  May be called again to move it.
+ * The calls of one plan write scratch state into its workspace, so they must run one
+ * after the other (one stream, or ordered by events); overlapping calls on one plan race. */
 qi_status qi_plan_upload(qi_plan *plan, void *d_workspace, size_t workspace_bytes,
                          void *stream);
 
@@ -183,19 +187,26 @@ qi_status qi_plan_tile_map(const qi_plan *plan, int32_t call, int32_t bm, int32_
 /* Tile shape (rows x keys) the attention kernel of a call uses; the tile map of the call
  * for this shape is the one the kernel follows.  To balance the last wave of workgroups
  * the launch schedule may run a row tile as two halves of at most bm/2 rows each (the
- * halves see the same key tiles, so the map is unchanged); the full call runs each row
+ * halves see the same key tiles, so the map is unchanged).  When the denoising call has
+ * fewer (row tile, head) items than the GPU has compute units (a head shard, e.g. 3 of 24
+ * heads), the plan instead cuts each row tile's keys into chunks of whole key tiles, one
+ * workgroup each, and a second kernel merges the chunks' partial softmax states in chunk
+ * order; the chunk length is one per plan.  Either way the full call runs each row
  * exactly as the prefix or denoising call runs it. */
 qi_status qi_plan_kernel_tile(const qi_plan *plan, int32_t call, int32_t *bm, int32_t *bn);
 
-/* The launch schedule of a call: one record of four int32 per workgroup, in launch order
- * (workgroup i runs on XCD i % 8): request, head, first row, row count.  The first row
- * is a position in the request's sequence (text, references, image; 0-based), so a
- * denoising item starts at L_p or later.  Padding workgroups, which do no work, read
- * -1 -1 -1 -1.  Row counts above half the kernel's row tile run on the kernel's
+/* The launch schedule of a call: one record of QI_LAUNCH_ITEM_FIELDS int32 per
+ * workgroup, in launch order (workgroup i runs on XCD i % 8): request, head, first row,
+ * row count, first key, end key.  The first row is a position in the request's sequence
+ * (text, references, image; 0-based), so a denoising item starts at L_p or later.  The
+ * workgroup visits keys [first key, end key) of the rows' visible keys: all of them, or
+ * one key chunk (see qi_plan_kernel_tile).  Padding workgroups, which do no work, read -1
+ * in every field.  Row counts above half the kernel's row tile run on the kernel's
  * whole-tile path; the others (half tiles the schedule split off, short block tails) run
  * with the key tiles split over two wavefront groups.  Writes into host_out (host
- * memory) when n >= 4 * workgroups; *n_needed (may be NULL) receives that count.
- * QI_ERR_BUFFER_TOO_SMALL if host_out is NULL or n is too small. */
+ * memory) when n >= QI_LAUNCH_ITEM_FIELDS * workgroups; *n_needed (may be NULL)
+ * receives that count.  QI_ERR_BUFFER_TOO_SMALL if host_out is NULL or n is too small. */
+#define QI_LAUNCH_ITEM_FIELDS 6
 qi_status qi_plan_launch_items(const qi_plan *plan, int32_t call, int32_t *host_out, size_t n,
                                size_t *n_needed);
 

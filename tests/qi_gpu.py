@@ -159,7 +159,7 @@ def sample_rows(bl, call, bm, rng, n_random, items=None, req=0):
     for r0, nr in tiles:
         rows.update({r0 - base, r0 + nr - 1 - base, r0 + min(nr - 1, 31) - base})
     if items is not None:
-        for r, _, r0, nr in items:
+        for r, _, r0, nr in items[:, :4]:
             if r != req:
                 continue
             for off in (0, 31, 32, 63, 64, nr - 1):

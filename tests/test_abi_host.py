@@ -161,23 +161,27 @@ def test_calls_rejected_before_any_launch():
 
 @pytest.mark.parametrize("reqs,h,d", WAVES)
 def test_launch_schedule_covers_every_row_once(reqs, h, d):
-    """Every (request, head, row) of a call is computed by exactly one workgroup; items
-    never cross a block and hold at most the kernel's row tile; the full call runs each
-    row in the same item shape as the prefix or denoising call (the reason reuse is
-    bit-exact); workgroup i runs on XCD i % 8, and items of one (request, head) stay on
-    one XCD."""
+    """Every (request, head, row, visible key) of a call is computed by exactly one
+    workgroup: items never cross a block and hold at most the kernel's row tile, and the
+    key chunks of one item tile its visible keys [0, end of its block) in whole 64-key
+    tiles; the full call runs each row in the same item shape and key chunks as the prefix
+    or denoising call (the reason reuse is bit-exact); workgroup i runs on XCD i % 8, and
+    without key chunks the items of one (request, head) stay on one XCD."""
     p = qi.Plan(reqs, h, d)
+    den = qi.qi_plan_launch_items(p, qi.QI_CALL_DENOISE)
+    split_plan = bool(np.any(den[:, 4] > 0))
     shapes = {}
     for call in (qi.QI_CALL_PREFIX, qi.QI_CALL_DENOISE, qi.QI_CALL_FULL):
         items = qi.qi_plan_launch_items(p, call)
-        bm, _ = qi.qi_plan_kernel_tile(p, call)
+        bm, bn = qi.qi_plan_kernel_tile(p, call)
         assert len(items) % 8 == 0
         pad = items[:, 0] < 0
         assert np.all(items[pad] == -1)
         seen = [np.zeros((sum(bl), h), np.int32) for bl in reqs]
         xcd = {}
+        chunks = {}
         for i, e in enumerate(items):
-            r, hh, r0, nr = (int(v) for v in e)
+            r, hh, r0, nr, k0, k1 = (int(v) for v in e)
             if r < 0:
                 continue
             bl = reqs[r]
@@ -188,13 +192,22 @@ def test_launch_schedule_covers_every_row_once(reqs, h, d):
                 assert b < len(bl) - 1
             elif call == qi.QI_CALL_DENOISE:
                 assert b == len(bl) - 1
+            if not split_plan:
+                assert xcd.setdefault((r, hh), i % 8) == i % 8
+            chunks.setdefault((r, hh, r0, nr), []).append((k0, k1))
+        for (r, hh, r0, nr), ks in chunks.items():
+            vis = int(np.cumsum(reqs[r])[np.searchsorted(np.cumsum(reqs[r]), r0, side="right")])
+            ks.sort()
+            assert ks[0][0] == 0 and ks[-1][1] == vis, (ks, vis)
+            for (a0, a1), (b0, _) in zip(ks, ks[1:]):
+                assert a1 == b0 and a1 % bn == 0, ks
+            assert all(a0 < a1 and a0 % bn == 0 for a0, a1 in ks)
             seen[r][r0:r0 + nr, hh] += 1
-            assert xcd.setdefault((r, hh), i % 8) == i % 8
             key = (r, hh, r0)
             if call == qi.QI_CALL_FULL:
-                assert shapes[key] == nr
+                assert shapes[key] == (nr, ks)
             else:
-                shapes[key] = nr
+                shapes[key] = (nr, ks)
         for r, bl in enumerate(reqs):
             lp = sum(bl[:-1])
             rows = {qi.QI_CALL_PREFIX: slice(0, lp), qi.QI_CALL_DENOISE: slice(lp, sum(bl)),
@@ -206,7 +219,34 @@ def test_launch_schedule_covers_every_row_once(reqs, h, d):
         qi.QI_ERR_INVALID_ARG
     assert qi.lib.qi_plan_launch_items(p.handle, 1, None, 0, ctypes.byref(n)) == \
         qi.QI_ERR_BUFFER_TOO_SMALL
-    assert n.value == 4 * len(qi.qi_plan_launch_items(p, 1))
+    assert n.value == qi.QI_LAUNCH_ITEM_FIELDS * len(qi.qi_plan_launch_items(p, 1))
+
+
+@pytest.mark.parametrize("reqs,h,split", [
+    ([[256] + [4096] * 5], 3, True),         # edit4 on one GPU's head shard (3 of 24 heads)
+    ([[512, 4096, 16384]], 3, True),         # edit2048, head shard
+    ([[256] + [4096] * 5], 24, False),       # edit4, all 24 heads: 384 items fill the chip
+    ([[256, 4096]], 24, False),              # t2i1024
+])
+def test_key_split_only_for_underfilled_plans(reqs, h, split):
+    """Keys are split only when the denoising call has fewer (row tile, head) items than
+    the GPU has compute units; chunks hold at least 8 key tiles (an item's last chunk may
+    be shorter) and fill whole rounds of one workgroup per CU closely (at least 90% of
+    the last round); the workspace grows by one partial state per (chunk, head) slot."""
+    p = qi.Plan(reqs, h, 128)
+    items = qi.qi_plan_launch_items(p, qi.QI_CALL_DENOISE)
+    live = items[items[:, 0] >= 0]
+    chunked = np.any(live[:, 4] > 0)
+    assert chunked == split
+    if split:
+        last = live[:, 5] == live[:, 5].max()
+        assert np.all((live[:, 5] - live[:, 4] >= 8 * 64) | last)
+        rounds = -(-len(live) // 256)
+        assert len(live) >= 0.9 * 256 * rounds, len(live)
+        per_xcd = np.bincount([i % 8 for i, e in enumerate(items) if e[0] >= 0], minlength=8)
+        assert per_xcd.max() <= 32 * rounds, per_xcd
+        slot_bytes = (256 * 128 + 2 * 256) * 4   # fp32 O of a 256-row tile, then m and l
+        assert p.workspace_bytes >= len(live) * slot_bytes
 
 
 def test_noalloc_build_rejects_plans_beyond_its_scratch():

@@ -130,7 +130,7 @@ def test_late_max_raise(gpu_device, kv, d):
     items = qi.qi_plan_launch_items(gw.plan, qi.QI_CALL_DENOISE)
     bm, _ = qi.qi_plan_kernel_tile(gw.plan, qi.QI_CALL_DENOISE)
     item_rows = np.zeros((w.image_lens[0], HEADS), np.int32)   # row count of each row's item
-    for r, h, r0, nr in items[items[:, 0] >= 0]:
+    for r, h, r0, nr in items[items[:, 0] >= 0][:, :4]:
         item_rows[r0 - lp:r0 - lp + nr, h] = nr
     prow = np.array([p[0] for p in plants])
     assert np.any(item_rows[prow] > bm // 2), "no planted row in a whole row tile"

@@ -181,11 +181,14 @@ def big():
     cache = {}
 
     def get(name):
+        """A named workload, or "<name>@h3": its head shard of three heads."""
         if name not in cache:
             cache.clear()
             torch.cuda.empty_cache()
             say("generating %s" % name)
-            cache[name] = synth.generate(name, steps=1)
+            base, _, shard = name.partition("@h")
+            w = synth.head_shard(base, int(shard)) if shard else base
+            cache[name] = synth.generate(w, steps=1)
         return cache[name]
     return get
 
@@ -209,11 +212,10 @@ def _sampled(gw, e, call, out, kv, n_random, seed, bar):
     return check(np.concatenate(got), np.concatenate(ref), *bar, what)
 
 
-@pytest.mark.parametrize("name", ["t2i1024", "edit4", "edit2048"])
-def test_full_size_bf16(gpu_device, big, name):
-    x = big(name)
-    gw = GpuWave(x, gpu_device)
-    say("%s: requests %s" % (name, gw.w.requests))
+def _full_size_bf16_check(gw, x):
+    """Sampled rows of build, denoise and full vs the oracle; denoise deterministic and
+    bit-identical to the full step's image rows; prefix rows of the full step equal to
+    the build; the bf16 cache a head-major copy of the prefix K/V."""
     o_pre = gw.build()
     o_img = gw.denoise()
     o_img2 = gw.denoise()
@@ -237,6 +239,54 @@ def test_full_size_bf16(gpu_device, big, name):
     voff = qi.qi_plan_cache_offset(gw.plan, 0, 1, 0, 0)
     vc = gw.cache[voff:voff + h * lp * d * 2].view(torch.bfloat16).view(h, lp, d)
     assert torch.equal(vc.view(torch.int16), gw.v_pre.transpose(0, 1).contiguous().view(torch.int16))
+
+
+@pytest.mark.parametrize("name", ["t2i1024", "edit4", "edit2048"])
+def test_full_size_bf16(gpu_device, big, name):
+    x = big(name)
+    gw = GpuWave(x, gpu_device)
+    say("%s: requests %s" % (name, gw.w.requests))
+    _full_size_bf16_check(gw, x)
+
+
+def _chunk_items(gw, call):
+    items = qi.qi_plan_launch_items(gw.plan, call)
+    live = items[items[:, 0] >= 0]
+    return live, int(np.sum(live[:, 4] > 0))
+
+
+@pytest.mark.parametrize("name", ["edit4", "edit2048"])
+def test_head_shard_bf16(gpu_device, big, name):
+    """One GPU's head shard (3 of 24 heads) at full length: too few (row tile, head)
+    items for the chip, so the plan cuts keys into chunks and merges them; the sampled
+    rows match the oracle and reuse stays bit-exact through the split."""
+    x = big(name + "@h3")
+    gw = GpuWave(x, gpu_device)
+    live, chunked = _chunk_items(gw, qi.QI_CALL_DENOISE)
+    say("%s@h3: %d denoising workgroups, %d of them later key chunks" % (name, len(live), chunked))
+    assert chunked > 0, "the head shard did not split keys"
+    _full_size_bf16_check(gw, x)
+
+
+@pytest.mark.parametrize("kv", ["fp8", "bf16"])
+def test_head_shard_wave8_request(gpu_device, kv):
+    """The wave8 request with the most references, alone, on a three-head shard: key
+    chunks over an fp8 (or bf16) cache, sampled rows against the oracle."""
+    refs = [len(b) - 2 for b in synth.WORKLOADS["wave8"].requests]
+    r = int(np.argmax(refs))
+    w = synth.head_shard("wave8", 3, requests=[r])
+    x = synth.generate(w, steps=1)
+    gw = GpuWave(x, gpu_device, kv=kv)
+    live, chunked = _chunk_items(gw, qi.QI_CALL_DENOISE)
+    assert chunked > 0
+    o_pre = gw.build()
+    o_img = gw.denoise()
+    o_img2 = gw.denoise()
+    torch.cuda.synchronize()
+    e = exact_inputs(x)
+    _sampled(gw, e, L.CALL_DENOISE, o_img, kv, 24, 8, (BF16_MAXABS, BF16_RELRMS))
+    _sampled(gw, e, L.CALL_PREFIX, o_pre, "bf16", 12, 9, (BF16_MAXABS, BF16_RELRMS))
+    assert torch.equal(o_img.view(torch.int16), o_img2.view(torch.int16)), "not deterministic"
 
 
 def test_full_size_wave8_fp8(gpu_device, big):

@@ -54,10 +54,13 @@ def test_noalloc_build_matches_ordinary_build(gpu_device, kv):
         n = gw.plan.cache_bytes
         assert torch.equal(gw_na.cache[:n], gw.cache[:n]), "cache bytes differ"
         assert torch.equal(bits(o_na), bits(o)), "prefix outputs differ"
-        # the allocation-free build never touched its workspace; the ordinary fp8 build
-        # keeps its partials there
-        assert torch.equal(gw_na.ws, s_na), "the allocation-free build wrote its workspace"
-        assert torch.equal(gw.ws, s) == (kv == "bf16")
+        # the allocation-free build writes no workspace byte the ordinary build leaves
+        # alone (both keep the partial softmax states of split key chunks there, when
+        # the plan splits keys); the ordinary fp8 build also keeps its absmax partials
+        # there, which the allocation-free one keeps in its static array
+        ch_na, ch = gw_na.ws != s_na, gw.ws != s
+        assert not torch.any(ch_na & ~ch), "the allocation-free build wrote outside the plan's state"
+        assert torch.any(ch & ~ch_na).item() == (kv != "bf16")
         d_na, d = gw_na.denoise(), gw.denoise()
         torch.cuda.synchronize()
         assert torch.equal(bits(d_na), bits(d)), "denoising outputs differ"
