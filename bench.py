@@ -376,11 +376,22 @@ def provenance():
         with open(f, "rb") as fh:
             h.update(os.path.basename(f).encode() + b"\0" + fh.read())
     props = torch.cuda.get_device_properties(0)
-    return {"device": torch.cuda.get_device_name(0),
+    name = torch.cuda.get_device_name(0)
+    if not name:   # some boxes report an empty name; the card's sysfs product name instead
+        for f in sorted(glob.glob("/sys/class/drm/card*/device/product_name")):
+            try:
+                with open(f) as fh:
+                    name = fh.read().strip()
+            except OSError:
+                continue
+            if name:
+                break
+    return {"device": name or None,
             "gcn_arch": getattr(props, "gcnArchName", None),
             "compute_units": props.multi_processor_count,
             "rocm": rocm, "torch_hip": torch.version.hip, "torch": torch.__version__,
-            "git_commit": git, "csrc_sha256": h.hexdigest()[:16]}
+            "git_commit": git,   # null where the tree has no .git (copies on a GPU machine)
+            "csrc_sha256": h.hexdigest()[:16]}
 
 
 def copy_calibration(nbytes):
