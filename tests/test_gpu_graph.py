@@ -20,16 +20,25 @@ from qi_gpu import BF16_MAXABS, BF16_RELRMS, GpuWave, check, exact_inputs, f64, 
 
 pytestmark = pytest.mark.gpu
 
-WAVE = [[40, 70, 96], [23, 129]]   # two requests, ragged blocks, one reference image
+WAVES = {
+    "ragged": [[40, 70, 96], [23, 129]],    # two requests, ragged blocks, one reference image
+    # 1700 keys on 2 heads: the plan cuts the keys into chunks, so the captured step holds
+    # the attention kernel and the merge of the chunks
+    "chunked": [[100, 700, 900]],
+}
 
 
 def bits(t):
     return t.view(torch.int16)
 
 
+@pytest.mark.parametrize("wave", sorted(WAVES))
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
-def test_graph_replay_matches_eager(gpu_device, kv):
-    layers = [GpuWave(synth.custom(WAVE, 2, 128, kv, seed=300 + l), gpu_device) for l in range(3)]
+def test_graph_replay_matches_eager(gpu_device, kv, wave):
+    layers = [GpuWave(synth.custom(WAVES[wave], 2, 128, kv, seed=300 + l), gpu_device)
+              for l in range(3)]
+    items = qi.qi_plan_launch_items(layers[0].plan, qi.QI_CALL_DENOISE)
+    assert bool((items[:, 4] > 0).any()) == (wave == "chunked")
     for gw in layers:
         gw.build()
     outs = [torch.empty_like(gw.img[0][0]) for gw in layers]
