@@ -70,7 +70,7 @@ int64_t item_cost(const qi_tile &t) {
 //     runs on XCD i % 8).
 void build_schedule(const qi_plan &p, std::vector<qi_tile> &tiles,
                     const std::vector<std::pair<int, int>> &items_in, int slots_per_xcd,
-                    bool may_split, std::vector<int32_t> &sched) {
+                    bool may_split, bool chunked, std::vector<int32_t> &sched) {
   std::vector<Unit> units;
   std::map<std::tuple<int, int, int, int>, int> unit_of;
   std::map<std::tuple<int, int, int>, int> run_len;
@@ -79,8 +79,8 @@ void build_schedule(const qi_plan &p, std::vector<qi_tile> &tiles,
     // head, chunk) cut into runs of at most 8 row tiles -- a head shard has too few
     // (request, head) pairs to spread over the XCDs
     int run = 0;
-    if (p.kchunk_tiles > 0) run = run_len[{tiles[t].req, h, tiles[t].k0}]++ / 8;
-    const auto key = std::make_tuple(tiles[t].req, h, p.kchunk_tiles > 0 ? tiles[t].k0 : 0, run);
+    if (chunked) run = run_len[{tiles[t].req, h, tiles[t].k0}]++ / 8;
+    const auto key = std::make_tuple(tiles[t].req, h, chunked ? tiles[t].k0 : 0, run);
     auto it = unit_of.find(key);
     if (it == unit_of.end()) {
       it = unit_of.emplace(key, (int)units.size()).first;
@@ -201,15 +201,15 @@ void build_tiles(const qi_plan &p, int call, std::vector<qi_tile> &tiles) {
 // Key tiles a row tile visits without a key split.
 int key_tiles(const qi_tile &t) { return (t.kend + QI_KERNEL_BN - 1) / QI_KERNEL_BN; }
 
-// Key split.  When the denoising call has fewer (row tile, head) items than compute units
-// (a head-sharded deployment: three heads of 24 per GPU), much of the chip would idle, so
-// every row tile's keys are cut into chunks of ct key tiles, each its own workgroup, and
-// the chunks' partial softmax states are merged afterwards.  ct minimises an estimate of
-// the call's time in key-tile units: rounds of one workgroup per CU times (the longest
-// chunk plus a workgroup's fixed cost), plus the merge's traffic per partial slot; the
-// split is taken only when that beats the whole row tiles by more than 5%.  0: no split.
-// One ct per plan: every call cuts a given row tile at the same keys, so reuse stays
-// bit-identical.
+// Key split.  When the prefix or the denoising call has fewer (row tile, head) items than
+// compute units (a head-sharded deployment: three heads of 24 per GPU), much of the chip
+// would idle, so every row tile's keys are cut into chunks of ct key tiles, each its own
+// workgroup, and the chunks' partial softmax states are merged afterwards.  ct minimises
+// an estimate of the call's time in key-tile units: rounds of one workgroup per CU times
+// (the longest chunk plus a workgroup's fixed cost), plus the merge's traffic per partial
+// slot; the split is taken only when that beats the whole row tiles by more than 5%.
+// 0: no split.  Each of the two calls picks its own ct; the full call runs every row in
+// the chunks of the call that owns the row, so reuse stays bit-identical.
 constexpr double kWgFixedTiles = 2.0;     // prologue (Q and first tiles) and epilogue
 constexpr double kMergeSlotTiles = 0.03;  // a slot's partial state written and read back
 double split_cost(const std::vector<qi_tile> &den, int H, int ct) {
@@ -393,15 +393,16 @@ qi_status qi_plan_create(const qi_wave_desc *d, qi_plan **out) {
     p->bm[c] = QI_ROWS;
     build_tiles(*p, c, tiles[c]);
   }
-  p->kchunk_tiles = choose_chunk_tiles(tiles[QI_CALL_DENOISE], p->H);
   for (int c : {QI_CALL_PREFIX, QI_CALL_DENOISE}) {
-    split_keys(p->kchunk_tiles, p->H, tiles[c], merges[c], merge_req[c], slots[c]);
+    p->kchunk_tiles[c] = choose_chunk_tiles(tiles[c], p->H);
+    split_keys(p->kchunk_tiles[c], p->H, tiles[c], merges[c], merge_req[c], slots[c]);
     std::vector<std::pair<int, int>> items;
     for (int t = 0; t < (int)tiles[c].size(); ++t)
       for (int h = 0; h < p->H; ++h) items.push_back({t, h});
     // the kernel runs one 8-wavefront workgroup per CU; key-split plans keep row tiles
     // whole (their chunks already fill the chip)
-    build_schedule(*p, tiles[c], items, QI_CUS_PER_XCD, p->kchunk_tiles == 0, sched[c]);
+    build_schedule(*p, tiles[c], items, QI_CUS_PER_XCD, p->kchunk_tiles[c] == 0,
+                   p->kchunk_tiles[c] > 0, sched[c]);
   }
   {
     p->bm[QI_CALL_FULL] = QI_ROWS;
@@ -446,7 +447,9 @@ qi_status qi_plan_create(const qi_wave_desc *d, qi_plan **out) {
         items.push_back({map[t], h});
       }
     }
-    build_schedule(*p, ft, items, QI_CUS_PER_XCD, false, sched[QI_CALL_FULL]);
+    build_schedule(*p, ft, items, QI_CUS_PER_XCD, false,
+                   p->kchunk_tiles[QI_CALL_PREFIX] > 0 || p->kchunk_tiles[QI_CALL_DENOISE] > 0,
+                   sched[QI_CALL_FULL]);
   }
   p->kpart_slots = std::max({slots[0], slots[1], slots[2]});
   size_t off = 0;

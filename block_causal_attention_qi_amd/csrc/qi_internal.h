@@ -54,8 +54,8 @@ static_assert(sizeof(qi_merge) == 16, "qi_merge is a 16-byte device record");
 // Partial slot of a key chunk: the unnormalised O of up to QI_ROWS rows ([row][D] fp32),
 // then the rows' running max m (log2 units) and sum l: (QI_ROWS * D + 2 * QI_ROWS) floats.
 #define QI_PART_SLOT_FLOATS(D) ((size_t)QI_ROWS * (D) + 2 * QI_ROWS)
-// Key chunks are used only when the denoising call has fewer (row tile, head) items than
-// compute units; a chunk holds at least this many key tiles.
+// Key chunks are used only in a prefix or denoising call with fewer (row tile, head) items
+// than compute units; a chunk holds at least this many key tiles.
 #define QI_SPLIT_MIN_TILES 8
 #define QI_NUM_CUS (QI_NUM_XCD * QI_CUS_PER_XCD)
 
@@ -93,9 +93,10 @@ struct qi_plan {
   int32_t bm[3] = {0, 0, 0};   // row tile size per call
   size_t reqs_off = 0, part_off = 0, part_floats = 0;
   int32_t max_chunks = 0;
-  // key split: chunk length in key tiles (0: none), merge tables per call, and the
-  // partial slots (shared by the calls, which run one after the other on a plan)
-  int32_t kchunk_tiles = 0;
+  // key split: chunk length in key tiles per call (0: none; the full call runs every row
+  // in its source call's chunks), merge tables per call, and the partial slots (shared by
+  // the calls, which run one after the other on a plan)
+  int32_t kchunk_tiles[3] = {0, 0, 0};
   size_t merge_off[3] = {0, 0, 0};
   int32_t n_merge[3] = {0, 0, 0};
   size_t kpart_off = 0;

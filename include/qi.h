@@ -187,12 +187,13 @@ qi_status qi_plan_tile_map(const qi_plan *plan, int32_t call, int32_t bm, int32_
 /* Tile shape (rows x keys) the attention kernel of a call uses; the tile map of the call
  * for this shape is the one the kernel follows.  To balance the last wave of workgroups
  * the launch schedule may run a row tile as two halves of at most bm/2 rows each (the
- * halves see the same key tiles, so the map is unchanged).  When the denoising call has
- * fewer (row tile, head) items than the GPU has compute units (a head shard, e.g. 3 of 24
- * heads), the plan instead cuts each row tile's keys into chunks of whole key tiles, one
- * workgroup each, and a second kernel merges the chunks' partial softmax states in chunk
- * order; the chunk length is one per plan.  Either way the full call runs each row
- * exactly as the prefix or denoising call runs it. */
+ * halves see the same key tiles, so the map is unchanged).  When the prefix or the
+ * denoising call has fewer (row tile, head) items than the GPU has compute units (a head
+ * shard, e.g. 3 of 24 heads), the plan instead cuts each of that call's row tiles' keys
+ * into chunks of whole key tiles, one workgroup each, and a second kernel merges the
+ * chunks' partial softmax states in chunk order; each of the two calls has one chunk
+ * length.  Either way the full call runs each row exactly as the prefix or denoising call
+ * runs it. */
 qi_status qi_plan_kernel_tile(const qi_plan *plan, int32_t call, int32_t *bm, int32_t *bn);
 
 /* The launch schedule of a call: one record of QI_LAUNCH_ITEM_FIELDS int32 per

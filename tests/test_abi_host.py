@@ -222,18 +222,29 @@ def test_launch_schedule_covers_every_row_once(reqs, h, d):
     assert n.value == qi.QI_LAUNCH_ITEM_FIELDS * len(qi.qi_plan_launch_items(p, 1))
 
 
-@pytest.mark.parametrize("reqs,h,split", [
-    ([[256] + [4096] * 5], 3, True),         # edit4 on one GPU's head shard (3 of 24 heads)
-    ([[512, 4096, 16384]], 3, True),         # edit2048, head shard
-    ([[256] + [4096] * 5], 24, False),       # edit4, all 24 heads: 384 items fill the chip
-    ([[256, 4096]], 24, False),              # t2i1024
+@pytest.mark.parametrize("reqs,h,split,pre_split", [
+    ([[256] + [4096] * 5], 3, True, True),     # edit4 on one GPU's head shard (3 of 24 heads)
+    ([[512, 4096, 16384]], 3, True, True),     # edit2048, head shard: 54 prefix items
+    ([[256] + [4096] * 5], 24, False, False),  # edit4, all 24 heads: 384 items fill the chip
+    ([[512, 4096, 16384]], 24, False, False),  # edit2048: 432 prefix items
+    ([[256, 4096]], 24, False, False),         # t2i1024: 24 prefix items of 4 key tiles
 ])
-def test_key_split_only_for_underfilled_plans(reqs, h, split):
-    """Keys are split only when the denoising call has fewer (row tile, head) items than
-    the GPU has compute units; chunks hold at least 8 key tiles (an item's last chunk may
-    be shorter) and fill whole rounds of one workgroup per CU closely (at least 90% of
-    the last round); the workspace grows by one partial state per (chunk, head) slot."""
+def test_key_split_only_for_underfilled_plans(reqs, h, split, pre_split):
+    """Keys are split only in a call with fewer (row tile, head) items than the GPU has
+    compute units (the prefix and denoising calls decide each for itself); chunks hold at
+    least 8 key tiles (an item's last chunk may be shorter) and a split denoising call
+    fills whole rounds of one workgroup per CU closely (at least 90% of the last round);
+    the workspace grows by one partial state per (chunk, head) slot."""
     p = qi.Plan(reqs, h, 128)
+    pre = qi.qi_plan_launch_items(p, qi.QI_CALL_PREFIX)
+    pre = pre[pre[:, 0] >= 0]
+    assert bool(np.any(pre[:, 4] > 0)) == pre_split
+    if pre_split:
+        # every chunk but an item's last holds >= 8 key tiles; the split at least doubles
+        # the workgroups of an underfilled call
+        for (r, hh, r0), ks in _chunks_of(pre).items():
+            assert all(k1 - k0 >= 8 * 64 for k0, k1 in ks[:-1]), ks
+        assert len(pre) >= 2 * len(_chunks_of(pre))
     items = qi.qi_plan_launch_items(p, qi.QI_CALL_DENOISE)
     live = items[items[:, 0] >= 0]
     chunked = np.any(live[:, 4] > 0)
@@ -247,6 +258,14 @@ def test_key_split_only_for_underfilled_plans(reqs, h, split):
         assert per_xcd.max() <= 32 * rounds, per_xcd
         slot_bytes = (256 * 128 + 2 * 256) * 4   # fp32 O of a 256-row tile, then m and l
         assert p.workspace_bytes >= len(live) * slot_bytes
+
+
+def _chunks_of(items):
+    """(request, head, first row) -> sorted key ranges of the item's workgroups."""
+    out = {}
+    for r, hh, r0, _nr, k0, k1 in items.tolist():
+        out.setdefault((r, hh, r0), []).append((k0, k1))
+    return {k: sorted(v) for k, v in out.items()}
 
 
 def test_noalloc_build_rejects_plans_beyond_its_scratch():
