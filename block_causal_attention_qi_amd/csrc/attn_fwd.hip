@@ -413,6 +413,14 @@ __device__ __forceinline__ void bar() { asm volatile("s_barrier" ::: "memory"); 
 // vmcnt (bits 3:0, 15:14) and expcnt (6:4) at their maxima).
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14)); }
 
+// Wait until at most N of this wavefront's vector-memory loads are outstanding (loads
+// complete in issue order); LDS and scalar-memory counters are left alone.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // ---------------------------------------------------------------------------------------
 // Per-wavefront pieces of one key tile.
 
@@ -914,7 +922,20 @@ __device__ __forceinline__ void pp_rows128(const Ring &r, const qi_tile &tl, int
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) acc[db][rr] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
-  __builtin_amdgcn_s_waitcnt(0);
+  if constexpr (FP8) {
+    __builtin_amdgcn_s_waitcnt(0);
+  } else {
+    // group 0: Q and K_0 (K_2, issued after them, is waited for at the end of its first
+    // VALU phase); group 1: Q only (K_1 and V_0 likewise)
+    constexpr int U = decltype(ld.dm)::U;
+    if (group == 0) {
+      if (n > 2) wait_vm<U>();
+      else wait_vm<0>();
+    } else {
+      if (n > 1) wait_vm<2 * U>();
+      else wait_vm<U>();
+    }
+  }
   bf16x8_t qf[C::QS];
   read_q_lds<D>(qst, qf);
   wait_lds();
