@@ -1043,12 +1043,15 @@ __global__ __launch_bounds__(NT, 1) void attn_pp_kernel(
 // Merge of key chunks: row (tile, head) gets O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M)
 // l_s over its chunks s in chunk order (M = max_s m_s), rounded to bf16 -- the same
 // combination the online softmax applies between key tiles, done once per chunk.  A
-// thread owns 4 dims of one row; a block covers RPB rows of one (tile, head).
+// thread owns 4 dims of one row; a block covers RPB rows of one (tile, head).  The loads
+// of up to MB chunks are issued together (entries past the last chunk reload the last one
+// and get weight 0, which leaves the sums exact); more chunks are folded MB at a time, the
+// running state rescaled by 2^(M_old - M_new) as between key tiles.
 template <int D>
 __global__ __launch_bounds__(256) void merge_chunks(const qi_merge *__restrict__ mg, int H,
                                                     const float *__restrict__ part,
                                                     __bf16 *__restrict__ o) {
-  constexpr int TPR = D / 4, RPB = 256 / TPR, BPT = QI_ROWS / RPB;
+  constexpr int TPR = D / 4, RPB = 256 / TPR, BPT = QI_ROWS / RPB, MB = 8;
   const int b = blockIdx.x;
   const int e = b / (H * BPT), h = (b / BPT) % H, rb = b % BPT;
   const qi_merge m = mg[e];
@@ -1056,20 +1059,40 @@ __global__ __launch_bounds__(256) void merge_chunks(const qi_merge *__restrict__
   if (row >= m.nrows) return;
   const int d = ((int)threadIdx.x % TPR) * 4;
   const size_t SLOT = QI_PART_SLOT_FLOATS(D), MO = (size_t)QI_ROWS * D;
-  float mx = -INFINITY;
-  for (int s = 0; s < m.nchunks; ++s)
-    mx = fmaxf(mx, part[(size_t)(m.part0 + s * H + h) * SLOT + MO + row]);
-  float l = 0.0f;
+  float mx = -INFINITY, l = 0.0f;
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  for (int s = 0; s < m.nchunks; ++s) {
-    const float *sl = part + (size_t)(m.part0 + s * H + h) * SLOT;
-    const float w = __builtin_amdgcn_exp2f(sl[MO + row] - mx);
-    l = __builtin_fmaf(w, sl[MO + QI_ROWS + row], l);
-    const float4 v = *reinterpret_cast<const float4 *>(sl + (size_t)row * D + d);
-    acc.x = __builtin_fmaf(w, v.x, acc.x);
-    acc.y = __builtin_fmaf(w, v.y, acc.y);
-    acc.z = __builtin_fmaf(w, v.z, acc.z);
-    acc.w = __builtin_fmaf(w, v.w, acc.w);
+  for (int s0 = 0; s0 < m.nchunks; s0 += MB) {
+    float ms[MB], ls[MB];
+    float4 os[MB];
+#pragma unroll
+    for (int j = 0; j < MB; ++j) {
+      const int sj = min(s0 + j, m.nchunks - 1);
+      const float *sl = part + (size_t)(m.part0 + sj * H + h) * SLOT;
+      ms[j] = sl[MO + row];
+      ls[j] = sl[MO + QI_ROWS + row];
+      os[j] = *reinterpret_cast<const float4 *>(sl + (size_t)row * D + d);
+    }
+    float mn = mx;
+#pragma unroll
+    for (int j = 0; j < MB; ++j) mn = fmaxf(mn, ms[j]);
+    if (s0 > 0) {   // chunks of earlier batches: rescale to the new maximum
+      const float a = __builtin_amdgcn_exp2f(mx - mn);
+      l *= a;
+      acc.x *= a;
+      acc.y *= a;
+      acc.z *= a;
+      acc.w *= a;
+    }
+    mx = mn;
+#pragma unroll
+    for (int j = 0; j < MB; ++j) {
+      const float w = s0 + j < m.nchunks ? __builtin_amdgcn_exp2f(ms[j] - mx) : 0.0f;
+      l = __builtin_fmaf(w, ls[j], l);
+      acc.x = __builtin_fmaf(w, os[j].x, acc.x);
+      acc.y = __builtin_fmaf(w, os[j].y, acc.y);
+      acc.z = __builtin_fmaf(w, os[j].z, acc.z);
+      acc.w = __builtin_fmaf(w, os[j].w, acc.w);
+    }
   }
   const float inv = 1.0f / l;
   uint2 u;

@@ -101,6 +101,9 @@ RAGGED = [
     ([[128, 128]], 1),
     ([[64, 64, 64], [127, 129, 257]], 2),
     ([[700, 1500, 900]], 2),
+    # one image row tile behind a 4000-token text: 2 items, keys cut into 9 chunks of 8
+    # key tiles, more than the merge takes in one batch
+    ([[4000, 200]], 2),
 ]
 
 
