@@ -26,6 +26,23 @@ WAVES = [
 ]
 
 
+def _random_small_head_waves(count=10, seed=77):
+    """Seeded ragged waves on 1..3 heads: few (row tile, head) items, so the prefix call,
+    the denoising call, both or neither cut their keys into chunks."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        reqs = []
+        for _ in range(int(rng.integers(1, 4))):
+            refs = [int(v) for v in rng.integers(1, 3001, int(rng.integers(0, 4)))]
+            reqs.append([int(rng.integers(1, 601))] + refs + [int(rng.integers(1, 3001))])
+        out.append((reqs, int(rng.integers(1, 4)), int(rng.choice([64, 128]))))
+    return out
+
+
+RANDOM_WAVES = _random_small_head_waves()
+
+
 def _declared():
     with open(os.path.join(ROOT, "include", "qi.h")) as f:
         text = f.read()
@@ -159,7 +176,7 @@ def test_calls_rejected_before_any_launch():
 
 
 
-@pytest.mark.parametrize("reqs,h,d", WAVES)
+@pytest.mark.parametrize("reqs,h,d", WAVES + RANDOM_WAVES)
 def test_launch_schedule_covers_every_row_once(reqs, h, d):
     """Every (request, head, row, visible key) of a call is computed by exactly one
     workgroup: items never cross a block and hold at most the kernel's row tile, and the
