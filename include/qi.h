@@ -129,9 +129,10 @@ qi_status qi_plan_upload(qi_plan *plan, void *d_workspace, size_t workspace_byte
  * step is what every later step reuses (ThakiCloud blog "Qwen-Image-2.1 vLLM-Omni day 0",
  * section "Serving architecture: the cross-step prefix KV cache"); the prefill runs once,
  * eagerly (vLLM recipe "Qwen/Qwen-Image-2.1", section "CUDA graphs"); FP8 storage is the
- * recipe's "fp8" / "fp8_v" option (section "Prefix KV cache").  q/k/v/o_pre: [sum L_p][H][D] bf16.  Fully overwrites
- * every request's region of d_cache (the cache is rebuilt per generation).  Requests
- * without a prefix cannot occur (the text block is never empty). */
+ * recipe's "fp8" / "fp8_v" option (section "Prefix KV cache").  q/k/v/o_pre:
+ * [sum L_p][H][D] bf16.  Fully overwrites every request's region of d_cache (the cache is
+ * rebuilt per generation).  Requests without a prefix cannot occur (the text block is
+ * never empty). */
 qi_status qi_prefix_kv_build(qi_plan *plan, const void *q_pre, const void *k_pre,
                              const void *v_pre, void *o_pre, void *d_cache,
                              size_t cache_bytes, void *stream);
@@ -156,8 +157,8 @@ qi_status qi_prefix_kv_build_noalloc(qi_plan *plan, const void *q_pre, const voi
  * live image keys of the same request -- the remaining steps reuse the cached prefix K/V
  * exactly and recompute only the image rows (vLLM recipe "Qwen/Qwen-Image-2.1", section
  * "Prefix KV cache"; ThakiCloud blog, section "Serving architecture: the cross-step prefix
- * KV cache"); requests at the same phase share one launch (recipe, "Online serving").  q/k/v/o_img: [sum N_img][H][D] bf16.  Reads the
- * cache only.  QI_ERR_STATE if no qi_prefix_kv_build has been enqueued on this plan.  On
+ * KV cache"); requests at the same phase share one launch (recipe, "Online serving").
+ * q/k/v/o_img: [sum N_img][H][D] bf16.  Reads the cache only.  QI_ERR_STATE if no qi_prefix_kv_build has been enqueued on this plan.  On
  * a bf16 cache the result is bit-identical to the image rows of
  * qi_attn_full_reference_step on the same values (same tiles, same arithmetic). */
 qi_status qi_denoise_attn_step(const qi_plan *plan, const void *d_cache, size_t cache_bytes,
