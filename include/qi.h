@@ -158,9 +158,10 @@ qi_status qi_prefix_kv_build_noalloc(qi_plan *plan, const void *q_pre, const voi
  * exactly and recompute only the image rows (vLLM recipe "Qwen/Qwen-Image-2.1", section
  * "Prefix KV cache"; ThakiCloud blog, section "Serving architecture: the cross-step prefix
  * KV cache"); requests at the same phase share one launch (recipe, "Online serving").
- * q/k/v/o_img: [sum N_img][H][D] bf16.  Reads the cache only.  QI_ERR_STATE if no qi_prefix_kv_build has been enqueued on this plan.  On
- * a bf16 cache the result is bit-identical to the image rows of
- * qi_attn_full_reference_step on the same values (same tiles, same arithmetic). */
+ * q/k/v/o_img: [sum N_img][H][D] bf16.  Reads the cache only.  QI_ERR_STATE if no
+ * qi_prefix_kv_build has been enqueued on this plan.  On a bf16 cache the result is
+ * bit-identical to the image rows of qi_attn_full_reference_step on the same values (same
+ * tiles, same arithmetic). */
 qi_status qi_denoise_attn_step(const qi_plan *plan, const void *d_cache, size_t cache_bytes,
                                const void *q_img, const void *k_img, const void *v_img,
                                void *o_img, void *stream);
@@ -170,8 +171,8 @@ qi_status qi_denoise_attn_step(const qi_plan *plan, const void *d_cache, size_t 
  * prefix cache cuts (about a fifth of the sequence is recomputed with four references:
  * vLLM recipe "Qwen/Qwen-Image-2.1", section "Prefix KV cache"), and the check that the
  * cached step is exact (ThakiCloud blog, section "Serving architecture: the cross-step
- * prefix KV cache": block-causal attention is what makes the reuse exact).  q/k/v/o_all: [sum N][H][D] bf16.  Used
- * to show that reuse is exact. */
+ * prefix KV cache": block-causal attention is what makes the reuse exact).
+ * q/k/v/o_all: [sum N][H][D] bf16.  Used to show that reuse is exact. */
 qi_status qi_attn_full_reference_step(const qi_plan *plan, const void *q_all,
                                       const void *k_all, const void *v_all, void *o_all,
                                       void *stream);
