@@ -60,7 +60,13 @@ int64_t item_cost(const qi_tile &t) {
 
 // Deal the (tile, head) items of a call to the XCDs and order them for launch.
 //  1. Units (request, head) go to XCDs longest-processing-time first, so the row tiles
-//     that stream one head's K/V run on one XCD and share its L2.
+//     that stream one head's K/V run on one XCD and share its L2.  When whole units
+//     cannot balance the XCDs (12 equal heads on 8 XCDs leave four XCDs with twice the
+//     work of the others), units are cut into runs of 32, 16, ... consecutive row tiles,
+//     keeping the cut that shortens the estimated launch (per XCD, the larger of its work
+//     over its workgroup slots and its longest item) by more than 2%, the first that comes
+//     within 2% of the lower bound; a head whose runs land on two XCDs is read into both
+//     L2s, a small cost next to an idle XCD.
 //  2. Per XCD the items are list-scheduled (longest first) on the XCD's workgroup slots.
 //     An item of more than 128 rows whose whole placement would end later than both the
 //     current makespan and the load-balance bound is split into its two 128-row halves
@@ -71,36 +77,70 @@ int64_t item_cost(const qi_tile &t) {
 void build_schedule(const qi_plan &p, std::vector<qi_tile> &tiles,
                     const std::vector<std::pair<int, int>> &items_in, int slots_per_xcd,
                     bool may_split, bool chunked, std::vector<int32_t> &sched) {
-  std::vector<Unit> units;
-  std::map<std::tuple<int, int, int, int>, int> unit_of;
-  std::map<std::tuple<int, int, int>, int> run_len;
-  for (auto [t, h] : items_in) {
-    // a unit shares one stream of K/V: (request, head), or with key chunks (request,
-    // head, chunk) cut into runs of at most 8 row tiles -- a head shard has too few
-    // (request, head) pairs to spread over the XCDs
-    int run = 0;
-    if (chunked) run = run_len[{tiles[t].req, h, tiles[t].k0}]++ / 8;
-    const auto key = std::make_tuple(tiles[t].req, h, chunked ? tiles[t].k0 : 0, run);
-    auto it = unit_of.find(key);
-    if (it == unit_of.end()) {
-      it = unit_of.emplace(key, (int)units.size()).first;
-      units.push_back(Unit{tiles[t].req, h, 0, {}});
+  using Bins = std::vector<std::vector<std::pair<int, int>>>;   // (tile, head) per XCD
+  // units of at most run_tiles row tiles, dealt to the XCDs longest first; returns the
+  // estimated launch length in item-cost units
+  auto deal = [&](int run_tiles, Bins &bins, std::vector<int64_t> &load) {
+    std::vector<Unit> units;
+    std::map<std::tuple<int, int, int, int>, int> unit_of;
+    std::map<std::tuple<int, int, int>, int> run_len;
+    for (auto [t, h] : items_in) {
+      // a unit shares one stream of K/V: (request, head), or with key chunks (request,
+      // head, chunk); cut into runs of consecutive row tiles
+      const int k0 = chunked ? tiles[t].k0 : 0;
+      const int run = run_len[{tiles[t].req, h, k0}]++ / run_tiles;
+      const auto key = std::make_tuple(tiles[t].req, h, k0, run);
+      auto it = unit_of.find(key);
+      if (it == unit_of.end()) {
+        it = unit_of.emplace(key, (int)units.size()).first;
+        units.push_back(Unit{tiles[t].req, h, 0, {}});
+      }
+      units[it->second].tiles.push_back(t);
+      units[it->second].cost += item_cost(tiles[t]);
     }
-    units[it->second].tiles.push_back(t);
-    units[it->second].cost += item_cost(tiles[t]);
-  }
-  for (Unit &u : units)
-    std::stable_sort(u.tiles.begin(), u.tiles.end(), [&](int a, int b) {
-      return item_cost(tiles[a]) > item_cost(tiles[b]);   // longest row tiles first
-    });
-  std::stable_sort(units.begin(), units.end(),
-                   [](const Unit &a, const Unit &b) { return a.cost > b.cost; });
-  std::vector<std::vector<std::pair<int, int>>> bins(QI_NUM_XCD);   // (tile, head)
-  std::vector<int64_t> load(QI_NUM_XCD, 0);
-  for (const Unit &u : units) {
-    int best = (int)(std::min_element(load.begin(), load.end()) - load.begin());
-    load[best] += u.cost;
-    for (int t : u.tiles) bins[best].push_back({t, u.head});
+    for (Unit &u : units)
+      std::stable_sort(u.tiles.begin(), u.tiles.end(), [&](int a, int b) {
+        return item_cost(tiles[a]) > item_cost(tiles[b]);   // longest row tiles first
+      });
+    std::stable_sort(units.begin(), units.end(),
+                     [](const Unit &a, const Unit &b) { return a.cost > b.cost; });
+    bins.assign(QI_NUM_XCD, {});
+    load.assign(QI_NUM_XCD, 0);
+    std::vector<int64_t> longest(QI_NUM_XCD, 0);
+    for (const Unit &u : units) {
+      int best = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+      load[best] += u.cost;
+      for (int t : u.tiles) {
+        bins[best].push_back({t, u.head});
+        longest[best] = std::max(longest[best], item_cost(tiles[t]));
+      }
+    }
+    int64_t est = 0;
+    for (int x = 0; x < QI_NUM_XCD; ++x)
+      est = std::max(est, std::max((load[x] + slots_per_xcd - 1) / slots_per_xcd, longest[x]));
+    return est;
+  };
+  // a head shard's key chunks: runs of at most 8 row tiles (too few (request, head) pairs
+  // to spread over the XCDs); otherwise whole units unless they leave the XCDs unbalanced
+  Bins bins;
+  std::vector<int64_t> load;
+  int64_t est = deal(chunked ? 8 : (1 << 30), bins, load);
+  if (!chunked) {
+    int64_t total = 0, longest = 0;
+    for (int64_t l : load) total += l;
+    for (auto [t, h] : items_in) longest = std::max(longest, item_cost(tiles[t]));
+    const int64_t slots = (int64_t)QI_NUM_XCD * slots_per_xcd;
+    const int64_t bound = std::max((total + slots - 1) / slots, longest);
+    for (int run_tiles = 32; run_tiles >= 1 && est * 50 > bound * 51; run_tiles /= 2) {
+      Bins b2;
+      std::vector<int64_t> l2;
+      const int64_t e2 = deal(run_tiles, b2, l2);
+      if (e2 * 51 < est * 50) {   // more than 2% shorter
+        est = e2;
+        bins.swap(b2);
+        load.swap(l2);
+      }
+    }
   }
   std::vector<std::vector<int32_t>> lists(QI_NUM_XCD);
   for (int x = 0; x < QI_NUM_XCD; ++x) {

@@ -183,7 +183,9 @@ def test_launch_schedule_covers_every_row_once(reqs, h, d):
     key chunks of one item tile its visible keys [0, end of its block) in whole 64-key
     tiles; the full call runs each row in the same item shape and key chunks as the prefix
     or denoising call (the reason reuse is bit-exact); workgroup i runs on XCD i % 8, and
-    without key chunks the items of one (request, head) stay on one XCD."""
+    without key chunks the items of one (request, head) stay on one XCD (these waves are
+    small enough that cutting a head's row tiles over XCDs would not shorten the launch;
+    see test_xcd_dealing_balances_head_shards)."""
     p = qi.Plan(reqs, h, d)
     den = qi.qi_plan_launch_items(p, qi.QI_CALL_DENOISE)
     split_plan = bool(np.any(den[:, 4] > 0))
@@ -275,6 +277,37 @@ def test_key_split_only_for_underfilled_plans(reqs, h, split, pre_split):
         assert per_xcd.max() <= 32 * rounds, per_xcd
         slot_bytes = (256 * 128 + 2 * 256) * 4   # fp32 O of a 256-row tile, then m and l
         assert p.workspace_bytes >= len(live) * slot_bytes
+
+
+def _xcd_loads(items):
+    """Work per XCD (key tiles x 128-row blocks) of a launch schedule (workgroup i on XCD
+    i % 8), and the XCDs each (request, head) runs on."""
+    load = np.zeros(8)
+    where = {}
+    for i, (r, hh, _r0, nr, k0, k1) in enumerate(items.tolist()):
+        if r < 0:
+            continue
+        load[i % 8] += ((k1 - k0 + 63) // 64) * ((nr + 127) // 128)
+        where.setdefault((r, hh), set()).add(i % 8)
+    return load, where
+
+
+@pytest.mark.parametrize("h", [6, 12, 24])
+def test_xcd_dealing_balances_head_shards(h):
+    """The 2048x2048 edit on 6 or 12 heads (a 4- or 2-way head split of 24): whole
+    (request, head) units cannot balance 8 XCDs (12 equal heads leave four XCDs with twice
+    the work), so the plan cuts them into runs of row tiles and every XCD gets the same
+    work within 2%; on 24 heads whole units already balance and each (request, head)
+    stays on one XCD, sharing its L2."""
+    p = qi.Plan([[512, 4096, 16384]], h, 128)
+    items = qi.qi_plan_launch_items(p, qi.QI_CALL_DENOISE)
+    assert not np.any(items[items[:, 0] >= 0][:, 4] > 0), "no key split at these sizes"
+    load, where = _xcd_loads(items)
+    assert load.max() <= 1.02 * load.mean(), load
+    if h == 24:
+        assert all(len(x) == 1 for x in where.values())
+    else:
+        assert any(len(x) > 1 for x in where.values())
 
 
 def _chunks_of(items):
